@@ -1,0 +1,439 @@
+// libpararnn.so — host side of the C ABI declared in include/pararnn.h:
+// argument checks, tiling plan, workspace layout and kernel dispatch.  No
+// entry point allocates, frees or synchronises; everything is enqueued on
+// the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "adjoint.hpp"
+#include "pararnn.h"
+#include "solve.hpp"
+
+using namespace pararnn;
+
+namespace {
+
+constexpr int64_t kMaxIters = 1 << 20;  // flag encoding leaves room below kStopBase
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+struct Plan {
+    int K = 0, W = 0;
+    int64_t P = 0, nb = 1;
+    int64_t channels = 0, units = 0;
+};
+
+int cell_S(pararnn_cell_t c) { return c == PARARNN_LSTM ? 2 : 1; }
+int cell_G(pararnn_cell_t c) { return c == PARARNN_LSTM ? 4 : 3; }
+int rec_floats(pararnn_cell_t c) { return c == PARARNN_LSTM ? MapRec<Map2>::kFloats : MapRec<Map1>::kFloats; }
+
+// Rows (b, d) of a [B][D][T]-style plane must not overlap: either d-major
+// inside b (stride_d >= T, stride_b >= D stride_d) or b-major inside d.
+bool rows_disjoint(int64_t B, int64_t T, int64_t D, int64_t sb, int64_t sd)
+{
+    if (sb < 0 || sd < 0) return false;
+    if (B <= 1 && D <= 1) return true;
+    if (B <= 1) return sd >= T;
+    if (D <= 1) return sb >= T;
+    return (sd >= T && sb >= D * sd) || (sb >= T && sd >= B * sb);
+}
+
+pararnn_status_t check_shape(const pararnn_shape_t *sh)
+{
+    if (!sh) return PARARNN_ERR_INVALID;
+    if (sh->B < 0 || sh->T < 0 || sh->D < 0) return PARARNN_ERR_INVALID;
+    if (sh->B > (int64_t(1) << 31) || sh->D > (int64_t(1) << 31) || sh->T > (int64_t(1) << 40))
+        return PARARNN_ERR_UNSUPPORTED;
+    if (!rows_disjoint(sh->B, sh->T, sh->D, sh->u_stride_b, sh->u_stride_d)) return PARARNN_ERR_INVALID;
+    if (!rows_disjoint(sh->B, sh->T, sh->D, sh->s_stride_b, sh->s_stride_d)) return PARARNN_ERR_INVALID;
+    return PARARNN_OK;
+}
+
+// Default tiling: the smallest block capacity P = 64 W K that covers T, from
+// a list ordered by preference; past the largest one, several time blocks
+// per channel.
+pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
+                           const pararnn_newton_t *opt, int adjoint, Plan &pl)
+{
+    pararnn_status_t st = check_shape(sh);
+    if (st != PARARNN_OK) return st;
+    int K = opt ? opt->steps_per_lane : 0;
+    int W = opt ? opt->waves_per_block : 0;
+    if ((K != 0 && !pow2_in(K, 1, 16)) || (W != 0 && !pow2_in(W, 1, 8)))
+        return PARARNN_ERR_UNSUPPORTED;
+    if (K == 0 || W == 0) {
+        static const int gru_kw[][2] = {{16, 4}, {16, 2}, {16, 1}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
+        static const int lstm_kw[][2] = {{8, 8}, {8, 4}, {8, 2}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
+        static const int adj_kw[][2] = {{8, 4}, {8, 2}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
+        const int(*tab)[2] = adjoint ? adj_kw : (cell == PARARNN_LSTM ? lstm_kw : gru_kw);
+        const int n = adjoint ? 6 : 7;
+        int pick = 0;
+        for (int i = 0; i < n; ++i) {
+            const int kk = K ? K : tab[i][0], ww = W ? W : tab[i][1];
+            if ((int64_t)kWave * kk * ww >= sh->T) pick = i;
+        }
+        if (K == 0) K = tab[pick][0];
+        if (W == 0) W = tab[pick][1];
+    }
+    pl.K = K;
+    pl.W = W;
+    pl.P = (int64_t)kWave * K * W;
+    pl.nb = sh->T > 0 ? (sh->T + pl.P - 1) / pl.P : 1;
+    pl.channels = sh->B * sh->D;
+    pl.units = pl.channels * pl.nb;
+    // dispatch packets count work-items in 32 bits
+    const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+    if (groups * kWave * W >= (int64_t(1) << 32)) return PARARNN_ERR_UNSUPPORTED;
+    if (pl.nb >= kStopBase) return PARARNN_ERR_UNSUPPORTED;
+    return PARARNN_OK;
+}
+
+struct SolveWs {
+    size_t ticket = 0, flags = 0, records = 0, hin0 = 0, total = 0;
+};
+
+SolveWs solve_ws_layout(pararnn_cell_t cell, const Plan &pl, const pararnn_newton_t *opt)
+{
+    SolveWs w;
+    if (pl.nb <= 1) return w;
+    const int64_t cap = opt ? opt->max_iters : 0;
+    size_t off = 0;
+    w.ticket = off;
+    off += kAlign;
+    w.flags = off;
+    off = align_up(off + (size_t)pl.units * sizeof(int32_t));
+    w.records = off;
+    off = align_up(off + (size_t)pl.units * (size_t)(cap + 1) * rec_floats(cell) * sizeof(float));
+    if (opt && opt->init_from_output) {
+        w.hin0 = off;
+        off = align_up(off + (size_t)pl.units * cell_S(cell) * sizeof(float));
+    }
+    w.total = off;
+    return w;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pararnn_status_t check_newton(const pararnn_newton_t *opt)
+{
+    if (!opt) return PARARNN_ERR_INVALID;
+    if (!(opt->tol >= 0.0f) || std::isinf(opt->tol)) return PARARNN_ERR_INVALID;
+    if (opt->max_iters < 0 || opt->max_iters > kMaxIters) return PARARNN_ERR_INVALID;
+    if (opt->init_from_output != 0 && opt->init_from_output != 1) return PARARNN_ERR_INVALID;
+    return PARARNN_OK;
+}
+
+#define PARARNN_KW_CASES(X)                                                                 \
+    X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 1) X(4, 2) X(4, 4)  \
+        X(4, 8) X(8, 1) X(8, 2) X(8, 4) X(8, 8) X(16, 1) X(16, 2) X(16, 4) X(16, 8)
+
+template <class Cell, bool BF16>
+hipError_t launch_newton(int K, int W, int64_t groups, hipStream_t st, const SolveArgs &a)
+{
+    const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));
+    switch (K * 100 + W) {
+#define X(KK, WW)                                                                           \
+    case KK * 100 + WW:                                                                     \
+        hipLaunchKernelGGL((newton_kernel<Cell, KK, WW, BF16>), grid, block, 0, st, a);     \
+        break;
+        PARARNN_KW_CASES(X)
+#undef X
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, const void *const *u,
+                              pararnn_dtype_t dt, const float *a, const float *const *s0,
+                              float *const *s, const pararnn_newton_t *opt, pararnn_info_t *info,
+                              void *ws, size_t ws_bytes, void *stream)
+{
+    pararnn_status_t st = check_newton(opt);
+    if (st != PARARNN_OK) return st;
+    Plan pl;
+    st = make_plan(cell, sh, opt, 0, pl);
+    if (st != PARARNN_OK) return st;
+    if (dt != PARARNN_F32 && dt != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;
+    const int G = cell_G(cell), S = cell_S(cell);
+    const bool work = pl.channels > 0 && sh->T > 0;
+    if (work) {
+        if (!u || !a || !s0 || !s) return PARARNN_ERR_INVALID;
+        for (int g = 0; g < G; ++g)
+            if (!u[g]) return PARARNN_ERR_INVALID;
+        for (int c = 0; c < S; ++c)
+            if (!s0[c] || !s[c]) return PARARNN_ERR_INVALID;
+    }
+    const SolveWs wl = solve_ws_layout(cell, pl, opt);
+    if (work && wl.total > 0 && (!ws || ws_bytes < wl.total || !aligned16(ws)))
+        return PARARNN_ERR_WORKSPACE;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+
+    SolveArgs A;
+    std::memset(&A, 0, sizeof(A));
+    for (int g = 0; g < G && work; ++g) A.u[g] = u[g];
+    A.a = a;
+    for (int c = 0; c < S && work; ++c) {
+        A.s0[c] = s0[c];
+        A.s[c] = s[c];
+    }
+    A.B = sh->B;
+    A.T = sh->T;
+    A.D = sh->D;
+    A.usb = sh->u_stride_b;
+    A.usd = sh->u_stride_d;
+    A.ssb = sh->s_stride_b;
+    A.ssd = sh->s_stride_d;
+    A.channels = pl.channels;
+    A.tol = opt->tol;
+    A.cap = opt->max_iters;
+    A.nb = (int32_t)pl.nb;
+    A.init_from_output = opt->init_from_output;
+    A.info = info;
+    const int ve = dt == PARARNN_BF16 ? 8 : 4;
+    bool uv = (sh->T % ve == 0) && (sh->u_stride_b % ve == 0) && (sh->u_stride_d % ve == 0);
+    for (int g = 0; g < G && work; ++g) uv = uv && aligned16(u[g]);
+    bool sv = (sh->T % 4 == 0) && (sh->s_stride_b % 4 == 0) && (sh->s_stride_d % 4 == 0);
+    for (int c = 0; c < S && work; ++c) sv = sv && aligned16(s[c]);
+    A.u_vec = uv ? 1 : 0;
+    A.s_vec = sv ? 1 : 0;
+    if (wl.total > 0) {
+        char *base = static_cast<char *>(ws);
+        A.ticket = reinterpret_cast<uint32_t *>(base + wl.ticket);
+        A.flags = reinterpret_cast<int32_t *>(base + wl.flags);
+        A.records = reinterpret_cast<float *>(base + wl.records);
+        A.hin0 = opt->init_from_output ? reinterpret_cast<float *>(base + wl.hin0) : nullptr;
+    }
+    if (!work) A.nb = 1;
+
+    const bool need_init = info != nullptr || (work && pl.nb > 1);
+    if (need_init) {
+        const int64_t n = (work && pl.nb > 1) ? pl.units : 1;
+        const int tpb = 256;
+        hipLaunchKernelGGL(solve_init_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
+                           strm, A, S, work ? pl.units : 0, (int32_t)pl.P);
+        if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    if (!work) return PARARNN_OK;
+    const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+    hipError_t e;
+    if (cell == PARARNN_GRU)
+        e = dt == PARARNN_BF16 ? launch_newton<GruCell, true>(pl.K, pl.W, groups, strm, A)
+                               : launch_newton<GruCell, false>(pl.K, pl.W, groups, strm, A);
+    else
+        e = dt == PARARNN_BF16 ? launch_newton<LstmCell, true>(pl.K, pl.W, groups, strm, A)
+                               : launch_newton<LstmCell, false>(pl.K, pl.W, groups, strm, A);
+    return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+}
+
+// ------------------------------------------------------------- adjoint ---
+
+struct AdjWs {
+    size_t ticket = 0, flags = 0, records = 0, da_part = 0, total = 0;
+};
+
+AdjWs adj_ws_layout(pararnn_cell_t cell, const Plan &pl)
+{
+    AdjWs w;
+    size_t off = 0;
+    w.ticket = off;
+    off += kAlign;
+    w.flags = off;
+    off = align_up(off + (size_t)pl.units * sizeof(int32_t));
+    w.records = off;
+    off = align_up(off + (size_t)pl.units * rec_floats(cell) * sizeof(float));
+    w.da_part = off;
+    off = align_up(off + (size_t)pl.units * cell_G(cell) * sizeof(float));
+    w.total = off;
+    return w;
+}
+
+template <class Cell, bool BF16>
+hipError_t launch_adjoint(int K, int W, int64_t groups, hipStream_t st, const AdjArgs &a)
+{
+    const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));
+    switch (K * 100 + W) {
+#define X(KK, WW)                                                                           \
+    case KK * 100 + WW:                                                                     \
+        hipLaunchKernelGGL((adjoint_kernel<Cell, KK, WW, BF16>), grid, block, 0, st, a);    \
+        break;
+        PARARNN_KW_CASES(X)
+#undef X
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pararnn_status_string(pararnn_status_t s)
+{
+    switch (s) {
+    case PARARNN_OK: return "ok";
+    case PARARNN_ERR_INVALID: return "invalid argument";
+    case PARARNN_ERR_UNSUPPORTED: return "unsupported argument combination";
+    case PARARNN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PARARNN_ERR_HIP: return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}
+
+pararnn_status_t pararnn_plan(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                              const pararnn_newton_t *opt, int adjoint, int32_t *K, int32_t *W,
+                              int64_t *nb)
+{
+    if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return PARARNN_ERR_INVALID;
+    Plan pl;
+    pararnn_status_t st = make_plan(cell, shape, opt, adjoint, pl);
+    if (st != PARARNN_OK) return st;
+    if (K) *K = pl.K;
+    if (W) *W = pl.W;
+    if (nb) *nb = pl.nb;
+    return PARARNN_OK;
+}
+
+size_t pararnn_workspace_bytes(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                               const pararnn_newton_t *opt, int adjoint)
+{
+    if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return 0;
+    Plan pl;
+    if (make_plan(cell, shape, opt, adjoint, pl) != PARARNN_OK) return 0;
+    if (adjoint) return adj_ws_layout(cell, pl).total;
+    if (opt && (opt->max_iters < 0 || opt->max_iters > kMaxIters)) return 0;
+    return solve_ws_layout(cell, pl, opt).total;
+}
+
+pararnn_status_t pararnn_solve_gru(const pararnn_shape_t *shape, const void *const u[3],
+                                   pararnn_dtype_t u_dtype, const float *a, const float *h0,
+                                   float *h, const pararnn_newton_t *opt, pararnn_info_t *info,
+                                   void *ws, size_t ws_bytes, void *stream)
+{
+    const float *s0[1] = {h0};
+    float *s[1] = {h};
+    return solve_common(PARARNN_GRU, shape, u, u_dtype, a, s0, s, opt, info, ws, ws_bytes, stream);
+}
+
+pararnn_status_t pararnn_solve_lstm(const pararnn_shape_t *shape, const void *const u[4],
+                                    pararnn_dtype_t u_dtype, const float *a, const float *c0,
+                                    const float *h0, float *c, float *h,
+                                    const pararnn_newton_t *opt, pararnn_info_t *info, void *ws,
+                                    size_t ws_bytes, void *stream)
+{
+    const float *s0[2] = {c0, h0};
+    float *s[2] = {c, h};
+    return solve_common(PARARNN_LSTM, shape, u, u_dtype, a, s0, s, opt, info, ws, ws_bytes, stream);
+}
+
+pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                                 const void *const *u, pararnn_dtype_t u_dtype, const float *a,
+                                 const float *const *s0, const float *const *s,
+                                 const float *const *gs, float *const *du, float *da,
+                                 float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
+                                 void *ws, size_t ws_bytes, void *stream)
+{
+    if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return PARARNN_ERR_INVALID;
+    if (u_dtype != PARARNN_F32 && u_dtype != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;
+    Plan pl;
+    pararnn_status_t st = make_plan(cell, shape, opt, 1, pl);
+    if (st != PARARNN_OK) return st;
+    const int G = cell_G(cell), S = cell_S(cell);
+    if (!da && shape->D > 0) return PARARNN_ERR_INVALID;
+    const bool work = pl.channels > 0 && shape->T > 0;
+    if (pl.channels > 0) {
+        if (!u || !s0 || !s || !gs || !du || !ds0 || !a) return PARARNN_ERR_INVALID;
+        for (int c = 0; c < S; ++c)
+            if (!s0[c] || !ds0[c] || (work && !s[c]) || (lam && !lam[c])) return PARARNN_ERR_INVALID;
+        for (int g = 0; g < G; ++g)
+            if (work && (!u[g] || !du[g])) return PARARNN_ERR_INVALID;
+    }
+    const AdjWs wl = adj_ws_layout(cell, pl);
+    if (!ws || ws_bytes < wl.total || !aligned16(ws)) return PARARNN_ERR_WORKSPACE;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+
+    AdjArgs A;
+    std::memset(&A, 0, sizeof(A));
+    for (int g = 0; g < G && pl.channels > 0; ++g) {
+        A.u[g] = work ? u[g] : nullptr;
+        A.du[g] = work ? du[g] : nullptr;
+    }
+    for (int c = 0; c < S && pl.channels > 0; ++c) {
+        A.s0[c] = s0[c];
+        A.s[c] = work ? s[c] : nullptr;
+        A.gs[c] = gs[c];
+        A.ds0[c] = ds0[c];
+        A.lam[c] = lam ? lam[c] : nullptr;
+    }
+    A.a = a;
+    A.da = da;
+    A.B = shape->B;
+    A.T = shape->T;
+    A.D = shape->D;
+    A.usb = shape->u_stride_b;
+    A.usd = shape->u_stride_d;
+    A.ssb = shape->s_stride_b;
+    A.ssd = shape->s_stride_d;
+    A.channels = pl.channels;
+    A.nb = (int32_t)pl.nb;
+    const int ve = u_dtype == PARARNN_BF16 ? 8 : 4;
+    bool uv = (shape->T % ve == 0) && (shape->u_stride_b % ve == 0) && (shape->u_stride_d % ve == 0);
+    bool dv = (shape->T % 4 == 0) && (shape->u_stride_b % 4 == 0) && (shape->u_stride_d % 4 == 0);
+    for (int g = 0; g < G && work; ++g) {
+        uv = uv && aligned16(u[g]);
+        dv = dv && aligned16(du[g]);
+    }
+    bool sv = (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) && (shape->s_stride_d % 4 == 0);
+    for (int c = 0; c < S && work; ++c) {
+        sv = sv && aligned16(s[c]);
+        if (gs[c]) sv = sv && aligned16(gs[c]);
+        if (lam) sv = sv && aligned16(lam[c]);
+    }
+    A.u_vec = uv ? 1 : 0;
+    A.du_vec = dv ? 1 : 0;
+    A.s_vec = sv ? 1 : 0;
+    char *base = static_cast<char *>(ws);
+    A.ticket = reinterpret_cast<uint32_t *>(base + wl.ticket);
+    A.flags = reinterpret_cast<int32_t *>(base + wl.flags);
+    A.records = reinterpret_cast<float *>(base + wl.records);
+    A.da_part = reinterpret_cast<float *>(base + wl.da_part);
+
+    if (pl.channels == 0) {
+        // nothing per channel; da over D = 0 channels is empty as well
+        return PARARNN_OK;
+    }
+    const int tpb = 256;
+    {
+        const int64_t n = pl.units;
+        hipLaunchKernelGGL(adjoint_init_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
+                           strm, A, S, G, pl.units);
+        if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    if (work) {
+        const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+        hipError_t e;
+        if (cell == PARARNN_GRU)
+            e = u_dtype == PARARNN_BF16 ? launch_adjoint<GruCell, true>(pl.K, pl.W, groups, strm, A)
+                                        : launch_adjoint<GruCell, false>(pl.K, pl.W, groups, strm, A);
+        else
+            e = u_dtype == PARARNN_BF16 ? launch_adjoint<LstmCell, true>(pl.K, pl.W, groups, strm, A)
+                                        : launch_adjoint<LstmCell, false>(pl.K, pl.W, groups, strm, A);
+        if (e != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    {
+        const int64_t n = (int64_t)G * shape->D;
+        hipLaunchKernelGGL(da_reduce_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0, strm,
+                           A, G);
+        if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    return PARARNN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+// Device primitives for the ParaRNN / DEER solve on gfx950 (CDNA4, wave64):
+// fast transcendentals, the affine maps the Newton systems are made of, and
+// wavefront-level scans built on DPP lane moves.
+//
+// Source of the scan structure: "Параллельность RNN?" (forpes.ru), §1.3,
+// level 2 — the linear recurrence ds_t = A_t ds_{t-1} + b_t is associative
+// because composing affine maps is; any bracketing of the composition gives
+// the same prefixes, so each channel's length-T recurrence is split into
+// per-lane serial chunks, a 64-lane wavefront scan, a scan over the waves of
+// a workgroup and a carry across workgroups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pararnn {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ----------------------------------------------------------- arithmetic ---
+
+__device__ __forceinline__ float fmaf_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+// v_exp_f32: 2^x.  v_rcp_f32: 1/x (1 ulp).  Both saturate cleanly:
+// 2^(+big) = +inf, 1/inf = 0, so the sigmoid/tanh forms below need no
+// clamping.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcpf_(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// sig(p) given q = -log2(e) * p.
+__device__ __forceinline__ float sigmoid_q(float q) { return rcpf_(1.0f + ex2(q)); }
+// tanh(p) given q = -2 log2(e) * p:  tanh p = 2 / (1 + e^{-2p}) - 1.
+__device__ __forceinline__ float tanh_q(float q) { return fmaf_(2.0f, rcpf_(1.0f + ex2(q)), -1.0f); }
+
+// |x| as an unsigned bit pattern.  For non-negative floats unsigned order is
+// float order and every NaN pattern is larger than +inf, so an unsigned max
+// over these never loses a NaN (IEEE fmax would).
+__device__ __forceinline__ uint32_t absbits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+// ---------------------------------------------------------- affine maps ---
+// A map x -> A x + b.  compose(L, E) applies E first, then L:
+//   (A_L, b_L) o (A_E, b_E) = (A_L A_E, A_L b_E + b_L).
+// apply() is the only place a map meets a vector: every carry in the
+// library goes through it, so two places that apply the same map to the
+// same vector get the same bits.
+
+struct Map1 {  // diagonal Jacobian (ParaGRU): 1x1 per channel
+    float a, b;
+};
+__device__ __forceinline__ Map1 identity_map(Map1) { return {1.0f, 0.0f}; }
+__device__ __forceinline__ Map1 compose(const Map1 &L, const Map1 &E)
+{
+    return {L.a * E.a, fmaf_(L.a, E.b, L.b)};
+}
+struct Vec1 {
+    float x;
+};
+__device__ __forceinline__ Vec1 apply(const Map1 &m, const Vec1 &v) { return {fmaf_(m.a, v.x, m.b)}; }
+
+struct Map2 {  // 2x2 block Jacobian (ParaLSTM), state order (c, h)
+    float a00, a01, a10, a11, b0, b1;
+};
+__device__ __forceinline__ Map2 identity_map(Map2) { return {1.0f, 0.0f, 0.0f, 1.0f, 0.0f, 0.0f}; }
+__device__ __forceinline__ Map2 compose(const Map2 &L, const Map2 &E)
+{
+    Map2 r;
+    r.a00 = fmaf_(L.a00, E.a00, L.a01 * E.a10);
+    r.a01 = fmaf_(L.a00, E.a01, L.a01 * E.a11);
+    r.a10 = fmaf_(L.a10, E.a00, L.a11 * E.a10);
+    r.a11 = fmaf_(L.a10, E.a01, L.a11 * E.a11);
+    r.b0 = fmaf_(L.a00, E.b0, fmaf_(L.a01, E.b1, L.b0));
+    r.b1 = fmaf_(L.a10, E.b0, fmaf_(L.a11, E.b1, L.b1));
+    return r;
+}
+struct Vec2 {
+    float x0, x1;
+};
+__device__ __forceinline__ Vec2 apply(const Map2 &m, const Vec2 &v)
+{
+    return {fmaf_(m.a00, v.x0, fmaf_(m.a01, v.x1, m.b0)),
+            fmaf_(m.a10, v.x0, fmaf_(m.a11, v.x1, m.b1))};
+}
+
+// ------------------------------------------------------------ DPP moves ---
+// update_dpp(old, src, ctrl, row_mask, bank_mask, bound_ctrl=false): lanes
+// whose source lane is out of range, or whose row is masked off, keep `old`.
+// GFX9 controls used: row_shr:n = 0x110+n, wave_shr:1 = 0x138,
+// row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ float dppf(float old, float src)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                      CTRL, RM, 0xF, false));
+}
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ uint32_t dppu(uint32_t old, uint32_t src)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, RM, 0xF, false);
+}
+
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ Map1 dpp_map(const Map1 &x)
+{
+    return {dppf<CTRL, RM>(1.0f, x.a), dppf<CTRL, RM>(0.0f, x.b)};
+}
+template <int CTRL, int RM = 0xF>
+__device__ __forceinline__ Map2 dpp_map(const Map2 &x)
+{
+    return {dppf<CTRL, RM>(1.0f, x.a00), dppf<CTRL, RM>(0.0f, x.a01),
+            dppf<CTRL, RM>(0.0f, x.a10), dppf<CTRL, RM>(1.0f, x.a11),
+            dppf<CTRL, RM>(0.0f, x.b0),  dppf<CTRL, RM>(0.0f, x.b1)};
+}
+
+// Inclusive scan over the 64 lanes in lane order: lane l ends with
+// x_l o x_{l-1} o ... o x_0.  Hillis-Steele inside each 16-lane row
+// (row_shr 1, 2, 4, 8), then row 0's total into row 1 and row 2's into
+// row 3 (row_bcast:15), then lanes 0..31's total into rows 2 and 3
+// (row_bcast:31).  Lanes that receive nothing compose with the identity.
+template <class M>
+__device__ __forceinline__ M wave_scan_inclusive(M x)
+{
+    x = compose(x, dpp_map<0x111>(x));
+    x = compose(x, dpp_map<0x112>(x));
+    x = compose(x, dpp_map<0x114>(x));
+    x = compose(x, dpp_map<0x118>(x));
+    x = compose(x, dpp_map<0x142, 0xA>(x));
+    x = compose(x, dpp_map<0x143, 0xC>(x));
+    return x;
+}
+
+// Value of lane l-1 (identity at lane 0): turns the inclusive scan into the
+// exclusive one.
+template <class M>
+__device__ __forceinline__ M wave_shift_up(const M &x) { return dpp_map<0x138>(x); }
+
+// Max over the 64 lanes, valid in lane 63 (same data movement as the scan).
+__device__ __forceinline__ uint32_t wave_max_to_last(uint32_t x)
+{
+    x = max(x, dppu<0x111>(0u, x));
+    x = max(x, dppu<0x112>(0u, x));
+    x = max(x, dppu<0x114>(0u, x));
+    x = max(x, dppu<0x118>(0u, x));
+    x = max(x, dppu<0x142, 0xA>(0u, x));
+    x = max(x, dppu<0x143, 0xC>(0u, x));
+    return x;
+}
+
+// Sum over the 64 lanes, valid in lane 63.
+__device__ __forceinline__ float wave_sum_to_last(float x)
+{
+    x += dppf<0x111>(0.0f, x);
+    x += dppf<0x112>(0.0f, x);
+    x += dppf<0x114>(0.0f, x);
+    x += dppf<0x118>(0.0f, x);
+    x += dppf<0x142, 0xA>(0.0f, x);
+    x += dppf<0x143, 0xC>(0.0f, x);
+    return x;
+}
+
+// ------------------------------------------------ device-scope flag ops ---
+__device__ __forceinline__ int32_t load_acquire(const int32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_release(int32_t *p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Payload words next to a flag are read with device-coherent relaxed loads
+// (vector memory, never the scalar cache) after an acquire on the flag.
+__device__ __forceinline__ float load_relaxed(const float *p)
+{
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void store_relaxed(float *p, float v)
+{
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace pararnn

@@ -1,0 +1,447 @@
+// Fused DEER Newton solve: one kernel runs, for every channel, the whole
+// Newton loop — residual and local Jacobian of the cell, parallel scan of the
+// resulting affine maps, state update and convergence test — with the
+// states, projections and per-step maps held in registers across iterations.
+// Only the projections are read from HBM (once) and only the converged
+// states are written (once).
+//
+// Method: "Параллельность RNN?" (forpes.ru), section 1.  Newton on the
+// residual r_t = s_t - f(s_{t-1}) (§1.1-1.2); each Newton system is the
+// block-bidiagonal forward substitution ds_t = A_t ds_{t-1} - r_t with
+// ds_1 = -r_1 (§1.3, level 1), solved as an associative scan of affine maps
+// (§1.3, level 2).  The fused single-kernel form is the "fully fused" tier
+// of the voguetech.ru ParaRNN article ("Три уровня производительности").
+//
+// Work decomposition for one channel (b, d) of length T:
+//   lane   : K consecutive steps, composed serially (up-sweep), later
+//            re-applied serially from the lane's carry-in (down-sweep);
+//   wave   : 64 lanes, inclusive scan of the lane aggregates via DPP;
+//   block  : W waves (P = 64 W K steps); wave aggregates go through LDS
+//            (double-buffered by iteration parity, one barrier/iteration);
+//   channel: ceil(T / P) time blocks; block k folds the aggregates its
+//            predecessors publish in global memory for the same iteration
+//            (decoupled: it waits only for their local work, not for a
+//            chain of prefixes).
+//
+// Every carry is applied with the same apply() on the same operands
+// wherever it is needed, so a lane's copy of its predecessor's last state
+// (h_{t0-1}) stays bitwise identical to the predecessor's own: no state
+// exchange between lanes, waves or blocks is ever needed.
+//
+// Stopping (per time block, causal): block k stops at iteration i iff its
+// max |r| < tol and every earlier block of the channel has stopped at or
+// before i; at the iteration cap every block stops.  With one block per
+// channel this is plain per-channel convergence.
+#pragma once
+
+#include "cells.hpp"
+#include "pararnn.h"
+
+namespace pararnn {
+
+constexpr int32_t kStopBase = 1 << 24;
+
+struct SolveArgs {
+    const void *u[4];
+    const float *a;
+    const float *s0[2];
+    float *s[2];
+    int64_t B, T, D;
+    int64_t usb, usd, ssb, ssd;
+    int64_t channels;
+    float tol;
+    int32_t cap;
+    int32_t nb;
+    int32_t init_from_output;
+    int32_t u_vec, s_vec;
+    uint32_t *ticket;
+    int32_t *flags;
+    float *records;
+    float *hin0;
+    pararnn_info_t *info;
+};
+
+template <class M>
+struct MapRec;
+template <>
+struct MapRec<Map1> {
+    static constexpr int kFloats = 4;  // a, b, cbit, pad
+};
+template <>
+struct MapRec<Map2> {
+    static constexpr int kFloats = 8;  // a00 a01 a10 a11 b0 b1 cbit pad
+};
+
+__device__ __forceinline__ void rec_store(float *r, const Map1 &m, uint32_t cbit)
+{
+    store_relaxed(r + 0, m.a);
+    store_relaxed(r + 1, m.b);
+    store_relaxed(r + 2, __uint_as_float(cbit));
+}
+__device__ __forceinline__ void rec_store(float *r, const Map2 &m, uint32_t cbit)
+{
+    store_relaxed(r + 0, m.a00);
+    store_relaxed(r + 1, m.a01);
+    store_relaxed(r + 2, m.a10);
+    store_relaxed(r + 3, m.a11);
+    store_relaxed(r + 4, m.b0);
+    store_relaxed(r + 5, m.b1);
+    store_relaxed(r + 6, __uint_as_float(cbit));
+}
+__device__ __forceinline__ void rec_load(const float *r, Map1 &m) { m = {load_relaxed(r), load_relaxed(r + 1)}; }
+__device__ __forceinline__ void rec_load(const float *r, Map2 &m)
+{
+    m = {load_relaxed(r),     load_relaxed(r + 1), load_relaxed(r + 2),
+         load_relaxed(r + 3), load_relaxed(r + 4), load_relaxed(r + 5)};
+}
+__device__ __forceinline__ uint32_t rec_cbit(const float *r, int n)
+{
+    return __float_as_uint(load_relaxed(r + n - 2));
+}
+
+// ------------------------------------------------------ vector plumbing ---
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// K consecutive steps t0..t0+K-1 of one plane, zero beyond T.  `vec` (uniform)
+// means T, the row strides and the base are multiples of 16 bytes, so 16-byte
+// vectors never straddle T.
+template <int K, bool BF16>
+__device__ __forceinline__ void load_steps(const void *base, int64_t off, int64_t t0, int64_t T,
+                                           bool vec, float (&out)[K])
+{
+    if constexpr (BF16) {
+        const uint16_t *p = static_cast<const uint16_t *>(base) + off;
+        if constexpr (K % 8 == 0) {
+            if (vec) {
+#pragma unroll
+                for (int q = 0; q < K / 8; ++q) {
+                    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                    if (t0 + 8 * q < T) v = *reinterpret_cast<const uint4 *>(p + t0 + 8 * q);
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        out[8 * q + 2 * j] = __uint_as_float(w[j] << 16);
+                        out[8 * q + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                    }
+                }
+                return;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) out[k] = (t0 + k < T) ? bf16_to_f32(p[t0 + k]) : 0.0f;
+    } else {
+        const float *p = static_cast<const float *>(base) + off;
+        if constexpr (K % 4 == 0) {
+            if (vec) {
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q) {
+                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (t0 + 4 * q < T) v = *reinterpret_cast<const float4 *>(p + t0 + 4 * q);
+                    out[4 * q] = v.x;
+                    out[4 * q + 1] = v.y;
+                    out[4 * q + 2] = v.z;
+                    out[4 * q + 3] = v.w;
+                }
+                return;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) out[k] = (t0 + k < T) ? p[t0 + k] : 0.0f;
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void store_steps(float *p, int64_t t0, int64_t T, bool vec,
+                                            const float (&v)[K])
+{
+    if constexpr (K % 4 == 0) {
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < K / 4; ++q)
+                if (t0 + 4 * q < T)
+                    *reinterpret_cast<float4 *>(p + t0 + 4 * q) =
+                        make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            return;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        if (t0 + k < T) p[t0 + k] = v[k];
+}
+
+template <class V>
+__device__ __forceinline__ V vzero();
+template <>
+__device__ __forceinline__ Vec1 vzero<Vec1>() { return {0.0f}; }
+template <>
+__device__ __forceinline__ Vec2 vzero<Vec2>() { return {0.0f, 0.0f}; }
+__device__ __forceinline__ Vec1 vadd(const Vec1 &a, const Vec1 &b) { return {a.x + b.x}; }
+__device__ __forceinline__ Vec2 vadd(const Vec2 &a, const Vec2 &b) { return {a.x0 + b.x0, a.x1 + b.x1}; }
+__device__ __forceinline__ float vget(const Vec1 &v, int) { return v.x; }
+__device__ __forceinline__ float vget(const Vec2 &v, int i) { return i ? v.x1 : v.x0; }
+__device__ __forceinline__ void vset(Vec1 &v, int, float x) { v.x = x; }
+__device__ __forceinline__ void vset(Vec2 &v, int i, float x)
+{
+    if (i)
+        v.x1 = x;
+    else
+        v.x0 = x;
+}
+
+// Maps (channel, time block) to a dynamic ticket so that block k-1 of a
+// channel always holds a smaller ticket than block k (it started earlier and
+// is resident or done: the waits below cannot deadlock).  Tickets 8 apart
+// belong to one channel, so when workgroups are spread round-robin over the
+// 8 XCDs the blocks of a channel tend to share an XCD and its L2.
+__device__ __forceinline__ void ticket_to_unit(int64_t t, int32_t nb, int64_t &ch, int32_t &k)
+{
+    const int64_t grp = 8 * (int64_t)nb;
+    const int64_t g = t / grp, r = t - g * grp;
+    k = (int32_t)(r >> 3);
+    ch = g * 8 + (r & 7);
+}
+
+// Look-back for time block k of channel `ch` at Newton iteration `it`:
+// returns the carry ds at the step before the block, and whether every
+// earlier block has stopped by `it`.
+template <class M, class V>
+__device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_t k, int32_t it,
+                                          V &din, bool &pred_stopped)
+{
+    constexpr int RF = MapRec<M>::kFloats;
+    const int32_t *flags = A.flags + ch * A.nb;
+    const float *rec = A.records + (ch * A.nb) * (int64_t)(A.cap + 1) * RF;
+    const int64_t rstride = (int64_t)(A.cap + 1) * RF;
+    // Pass 1: walk back to the nearest block that stopped at or before `it`
+    // (every block before it stopped no later), waiting for each one's
+    // record of this iteration.
+    int32_t start = 0;
+    for (int32_t j = k - 1; j >= 0; --j) {
+        int32_t v = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        while (v < it + 1) {
+            __builtin_amdgcn_s_sleep(2);
+            v = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (v >= kStopBase && v - kStopBase <= it) {
+            start = j + 1;
+            break;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // Pass 2: blocks start..p-1 all report |r| < tol at `it`, so they stop
+    // now (their carry-out is zero); the carry is the fold of p..k-1.
+    int32_t p = start;
+    while (p < k && rec_cbit(rec + p * rstride + it * RF, RF)) ++p;
+    pred_stopped = (p == k);
+    din = vzero<V>();
+    for (int32_t j = p; j < k; ++j) {
+        M m;
+        rec_load(rec + j * rstride + it * RF, m);
+        din = apply(m, din);
+    }
+}
+
+template <class M>
+struct Slot {
+    M agg;
+    uint32_t mx;
+};
+
+template <class Cell, int K, int W, bool BF16>
+__global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
+{
+    using M = typename Cell::Map;
+    using V = typename Cell::Vec;
+    constexpr int G = Cell::G, S = Cell::S;
+    constexpr int P = W * kWave * K;
+    constexpr int RF = MapRec<M>::kFloats;
+
+    __shared__ Slot<M> slots[2][W];
+    __shared__ int64_t s_ticket;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+
+    int64_t ch;
+    int32_t k;
+    if (A.nb > 1) {
+        if (threadIdx.x == 0) s_ticket = (int64_t)atomicAdd(A.ticket, 1u);
+        __syncthreads();
+        ticket_to_unit(s_ticket, A.nb, ch, k);
+    } else {
+        ch = blockIdx.x;
+        k = 0;
+    }
+    if (ch >= A.channels) return;
+    const int64_t unit = ch * A.nb + k;
+    const int64_t b = ch / A.D, d = ch - b * A.D;
+    const int64_t T = A.T;
+    const int64_t tb0 = (int64_t)k * P;
+    const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
+    const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
+
+    const typename Cell::Coef cf = Cell::coef(A.a, A.D, d);
+
+    // Projections, pre-scaled for the exp2-based gates.
+    float u[K][G];
+    {
+        const int64_t uoff = b * A.usb + d * A.usd;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float tmp[K];
+            load_steps<K, BF16>(A.u[g], uoff, t0, T, A.u_vec != 0, tmp);
+            const float sc = Cell::uscale(g);
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) u[kk][g] = tmp[kk] * sc;
+        }
+    }
+
+    // Newton start and the lane's copy of the state just before it.
+    const int64_t soff = b * A.ssb + d * A.ssd;
+    V s[K];
+    V hin;
+    if (A.init_from_output) {
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+            float tmp[K];
+            load_steps<K, false>(A.s[c], soff, t0, T, A.s_vec != 0, tmp);
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) vset(s[kk], c, tmp[kk]);
+        }
+        hin = vzero<V>();
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+            float x = 0.0f;
+            if (t0 == 0)
+                x = A.s0[c][b * A.D + d];
+            else if (t0 == tb0)
+                x = A.hin0[unit * S + c];
+            else if (t0 - 1 < T)
+                x = A.s[c][soff + t0 - 1];
+            vset(hin, c, x);
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) s[kk] = vzero<V>();
+        hin = vzero<V>();
+        if (t0 == 0) {
+#pragma unroll
+            for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
+        }
+    }
+
+    const uint32_t tolb = __float_as_uint(A.tol);
+    M m[K];
+    int32_t it = 0;
+    uint32_t bmx = 0;
+    for (;; ++it) {
+        // ---- residual, Jacobian and lane up-sweep
+        uint32_t mx = 0;
+        M agg = identity_map(M{});
+        V prev = hin;
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) {
+            if (t0 + kk < T)
+                m[kk] = Cell::step_map(cf, u[kk], prev, s[kk], mx);
+            else
+                m[kk] = identity_map(M{});
+            prev = s[kk];
+            agg = kk == 0 ? m[0] : compose(m[kk], agg);
+        }
+        // ---- wave scan, then block exchange through LDS
+        const M inc = wave_scan_inclusive(agg);
+        const M exc = wave_shift_up(inc);
+        const uint32_t wmx = wave_max_to_last(mx);
+        const int par = it & 1;
+        if (lane == kWave - 1) {
+            slots[par][wave].agg = inc;
+            slots[par][wave].mx = wmx;
+        }
+        __syncthreads();
+        bmx = slots[par][0].mx;
+        M blk = slots[par][0].agg;
+#pragma unroll
+        for (int j = 1; j < W; ++j) {
+            bmx = max(bmx, slots[par][j].mx);
+            blk = compose(slots[par][j].agg, blk);
+        }
+        const uint32_t cbit = bmx < tolb ? 1u : 0u;
+        const bool at_cap = (it == A.cap);
+        if (A.nb > 1 && threadIdx.x == 0) {
+            rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
+            store_release(A.flags + unit, it + 1);
+        }
+        if (at_cap) break;
+        V din = vzero<V>();
+        bool pred_stopped = true;
+        if (k > 0) look_back<M, V>(A, ch, k, it, din, pred_stopped);
+        if (cbit && pred_stopped) {
+            if (A.nb > 1 && threadIdx.x == 0) store_release(A.flags + unit, kStopBase + it);
+            break;
+        }
+        // ---- down-sweep from the carries, Newton update
+        V dw = din;
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j)
+            if (j < wave) dw = apply(slots[par][j].agg, dw);
+        const V dl = apply(exc, dw);
+        const V dout = (A.nb > 1 && last_lane_of_block) ? apply(blk, din) : apply(inc, dw);
+        hin = vadd(hin, dl);
+        V dd = dl;
+#pragma unroll
+        for (int kk = 0; kk < K - 1; ++kk) {
+            dd = apply(m[kk], dd);
+            s[kk] = vadd(s[kk], dd);
+        }
+        s[K - 1] = vadd(s[K - 1], dout);
+    }
+
+    // ---- converged states out
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        float tmp[K];
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) tmp[kk] = vget(s[kk], c);
+        store_steps<K>(A.s[c] + soff, t0, T, A.s_vec != 0, tmp);
+    }
+    if (A.info && threadIdx.x == 0) {
+        pararnn_info_t *inf = A.info;
+        atomicMax(&inf->iters, it);
+        if (!(bmx < tolb)) atomicAnd(&inf->converged, 0);
+        atomicMax(reinterpret_cast<unsigned int *>(&inf->max_abs_res), bmx);
+        if (bmx > 0x7f800000u) atomicOr(&inf->nan_seen, 1);
+        atomicAdd(reinterpret_cast<unsigned long long *>(&inf->iters_sum),
+                  (unsigned long long)it);
+    }
+}
+
+// Clears the per-launch state (ticket counter, block flags, info record) and
+// gathers the initial boundary states a warm-started multi-block solve needs.
+__global__ void solve_init_kernel(SolveArgs A, int32_t S, int64_t units, int32_t P)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) {
+        if (A.ticket) *A.ticket = 0u;
+        if (A.info) {
+            A.info->iters = 0;
+            A.info->converged = 1;
+            A.info->max_abs_res = 0.0f;
+            A.info->nan_seen = 0;
+            A.info->iters_sum = 0;
+            A.info->units = units;
+        }
+    }
+    if (i < units && A.flags) {
+        A.flags[i] = 0;
+        if (A.init_from_output && A.hin0) {
+            const int64_t ch = i / A.nb;
+            const int32_t k = (int32_t)(i - ch * A.nb);
+            const int64_t b = ch / A.D, d = ch - b * A.D;
+            for (int c = 0; c < S; ++c)
+                A.hin0[i * S + c] = k > 0 ? A.s[c][b * A.ssb + d * A.ssd + (int64_t)k * P - 1] : 0.0f;
+        }
+    }
+}
+
+}  // namespace pararnn

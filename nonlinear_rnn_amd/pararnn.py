@@ -1,0 +1,274 @@
+"""Python binding of libpararnn.so (argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI of
+``include/pararnn.h``; this module only turns torch tensors (device memory)
+and the current HIP stream into the pointers and sizes the ABI takes, and
+raises on a non-OK status.  There is no fallback: if the library or a GPU
+is missing, the calls raise.
+
+Names follow the ABI: ``solve_gru``, ``solve_lstm``, ``adjoint``,
+``workspace_bytes``, ``plan``.
+"""
+import ctypes
+import os
+import struct
+
+import torch  # loads the HIP runtime the library then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpararnn.so")
+
+GRU, LSTM = 0, 1
+F32, BF16 = 0, 1
+CELLS = {"gru": GRU, "lstm": LSTM}
+N_GATES = {GRU: 3, LSTM: 4}
+N_STATES = {GRU: 1, LSTM: 2}
+
+
+class PararnnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"pararnn status {status}: {msg}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("u_stride_b", ctypes.c_int64), ("u_stride_d", ctypes.c_int64),
+                ("s_stride_b", ctypes.c_int64), ("s_stride_d", ctypes.c_int64)]
+
+
+class Newton(ctypes.Structure):
+    _fields_ = [("tol", ctypes.c_float), ("max_iters", ctypes.c_int32),
+                ("steps_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+                ("init_from_output", ctypes.c_int32)]
+
+
+INFO_BYTES = 32
+_INFO_FMT = "<iifiqq"
+
+_lib = None
+
+
+def load():
+    """Load libpararnn.so (after torch, so both use one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m nonlinear_rnn_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    P = ctypes.POINTER
+    lib.pararnn_status_string.restype = ctypes.c_char_p
+    lib.pararnn_status_string.argtypes = [i32]
+    lib.pararnn_workspace_bytes.restype = sz
+    lib.pararnn_workspace_bytes.argtypes = [i32, P(Shape), P(Newton), i32]
+    lib.pararnn_plan.restype = i32
+    lib.pararnn_plan.argtypes = [i32, P(Shape), P(Newton), i32, P(ctypes.c_int32),
+                                 P(ctypes.c_int32), P(ctypes.c_int64)]
+    lib.pararnn_solve_gru.restype = i32
+    lib.pararnn_solve_gru.argtypes = [P(Shape), vp, i32, vp, vp, vp, P(Newton), vp, vp, sz, vp]
+    lib.pararnn_solve_lstm.restype = i32
+    lib.pararnn_solve_lstm.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, P(Newton), vp,
+                                       vp, sz, vp]
+    lib.pararnn_adjoint.restype = i32
+    lib.pararnn_adjoint.argtypes = [i32, P(Shape), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    P(Newton), vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pararnn_status_string(status).decode()
+
+
+def _check(status):
+    if status != 0:
+        raise PararnnError(status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def _strides(planes, name):
+    st = None
+    for p in planes:
+        if p is None:
+            continue
+        if p.dim() != 3:
+            raise ValueError(f"{name}: planes must be [B][D][T]")
+        if p.numel() == 0:
+            continue
+        if p.stride(2) != 1:
+            raise ValueError(f"{name}: planes must be [B][D][T] with time contiguous")
+        s = (p.stride(0), p.stride(1))
+        if st is not None and s != st:
+            raise ValueError(f"{name}: all planes must share strides")
+        st = s
+    return st
+
+
+def make_shape(B, T, D, u_strides=None, s_strides=None):
+    us = u_strides or (D * T, T)
+    ss = s_strides or (D * T, T)
+    return Shape(B, T, D, us[0], us[1], ss[0], ss[1])
+
+
+def make_newton(tol=1e-6, max_iters=20, steps_per_lane=0, waves_per_block=0,
+                init_from_output=False):
+    return Newton(float(tol), int(max_iters), int(steps_per_lane), int(waves_per_block),
+                  1 if init_from_output else 0)
+
+
+def workspace_bytes(cell, shape, newton=None, adjoint=False):
+    cell = CELLS.get(cell, cell)
+    return int(load().pararnn_workspace_bytes(cell, ctypes.byref(shape),
+                                              ctypes.byref(newton) if newton else None,
+                                              1 if adjoint else 0))
+
+
+def plan(cell, shape, newton=None, adjoint=False):
+    """(steps per lane K, waves per block W, time blocks per channel)."""
+    cell = CELLS.get(cell, cell)
+    K, W, nb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(load().pararnn_plan(cell, ctypes.byref(shape),
+                               ctypes.byref(newton) if newton else None, 1 if adjoint else 0,
+                               ctypes.byref(K), ctypes.byref(W), ctypes.byref(nb)))
+    return K.value, W.value, nb.value
+
+
+def decode_info(raw) -> dict:
+    it, conv, mres, nan, isum, units = struct.unpack(_INFO_FMT, bytes(raw))
+    return dict(iters=it, converged=bool(conv), max_abs_res=mres, nan_seen=bool(nan),
+                iters_sum=isum, units=units, iters_mean=(isum / units) if units else 0.0)
+
+
+class Workspace:
+    """Grow-only device scratch buffer (torch-allocated), one per device."""
+
+    def __init__(self):
+        self.buf = {}
+
+    def get(self, nbytes, device):
+        if nbytes == 0:
+            return None
+        key = torch.device(device).index
+        b = self.buf.get(key)
+        if b is None or b.numel() < nbytes:
+            b = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            self.buf[key] = b
+        return b
+
+
+_ws = Workspace()
+
+
+def _stream_handle(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _u_dtype(planes):
+    dts = {p.dtype for p in planes}
+    if dts == {torch.float32}:
+        return F32
+    if dts == {torch.bfloat16}:
+        return BF16
+    raise ValueError("u planes must all be float32 or all bfloat16")
+
+
+def _solve(cell, u, a, s0, out, tol, max_iters, steps_per_lane, waves_per_block,
+           init_from_output, info, workspace, stream):
+    lib = load()
+    G, S = N_GATES[cell], N_STATES[cell]
+    if len(u) != G or len(s0) != S:
+        raise ValueError("wrong number of gate or state planes")
+    B, D, T = u[0].shape
+    dev = u[0].device
+    if out is None:
+        out = [torch.empty((B, D, T), dtype=torch.float32, device=dev) for _ in range(S)]
+        if init_from_output:
+            raise ValueError("init_from_output needs the output planes")
+    shape = make_shape(B, T, D, _strides(u, "u"), _strides(out, "states"))
+    newton = make_newton(tol, max_iters, steps_per_lane, waves_per_block, init_from_output)
+    nws = workspace_bytes(cell, shape, newton)
+    ws = workspace if workspace is not None else _ws.get(nws, dev)
+    info_t = torch.empty(INFO_BYTES, dtype=torch.uint8, device=dev) if info else None
+    args = [ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a)]
+    args += [_ptr(x) for x in s0] + [_ptr(x) for x in out]
+    args += [ctypes.byref(newton), _ptr(info_t), _ptr(ws),
+             0 if ws is None else ws.numel(), _stream_handle(stream)]
+    fn = lib.pararnn_solve_gru if cell == GRU else lib.pararnn_solve_lstm
+    _check(fn(*args))
+    return out, info_t
+
+
+def solve_gru(u, a, h0, *, out=None, tol=1e-6, max_iters=20, steps_per_lane=0,
+              waves_per_block=0, init_from_output=False, info=True, workspace=None,
+              stream=None):
+    """ParaGRU Newton solve.  u = [u_z, u_r, u_c] device tensors [B][D][T]
+    (float32 or bfloat16), a [3][D] float32, h0 [B][D] float32.  Returns
+    (h, info_tensor) with info_tensor a 32-byte device buffer (or None);
+    ``read_info(info_tensor)`` synchronises and decodes it."""
+    out = None if out is None else [out]
+    s, info_t = _solve(GRU, list(u), a, [h0], out, tol, max_iters, steps_per_lane,
+                       waves_per_block, init_from_output, info, workspace, stream)
+    return s[0], info_t
+
+
+def solve_lstm(u, a, c0, h0, *, out=None, tol=1e-6, max_iters=20, steps_per_lane=0,
+               waves_per_block=0, init_from_output=False, info=True, workspace=None,
+               stream=None):
+    """ParaLSTM Newton solve.  u = [u_i, u_f, u_g, u_o]; a [4][D]; c0, h0
+    [B][D].  Returns ((c, h), info_tensor)."""
+    s, info_t = _solve(LSTM, list(u), a, [c0, h0], out, tol, max_iters, steps_per_lane,
+                       waves_per_block, init_from_output, info, workspace, stream)
+    return (s[0], s[1]), info_t
+
+
+def read_info(info_t) -> dict:
+    torch.cuda.current_stream(info_t.device).synchronize()
+    return decode_info(info_t.cpu().numpy().tobytes())
+
+
+def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
+            waves_per_block=0, workspace=None, stream=None):
+    """Backward pass of a converged solve for L = sum_t <gs_t, s_t>.
+    cell "gru" (s0, s, gs: [h]) or "lstm" ([c, h]); an entry of gs may be
+    None (zero).  Returns dict(du=[G planes], da [G][D], ds0=[S], lam=[S] or
+    None), all float32 device tensors."""
+    lib = load()
+    cell = CELLS.get(cell, cell)
+    G, S = N_GATES[cell], N_STATES[cell]
+    u, s0, s, gs = list(u), list(s0), list(s), list(gs)
+    if len(u) != G or len(s0) != S or len(s) != S or len(gs) != S:
+        raise ValueError("wrong number of gate or state planes")
+    B, D, T = u[0].shape
+    dev = u[0].device
+    us = _strides(u, "u")
+    ss = _strides(s + [g for g in gs if g is not None], "states")
+    du = [torch.empty_strided((B, D, T), (us[0], us[1], 1), dtype=torch.float32, device=dev)
+          for _ in range(G)]
+    da = torch.empty((G, D), dtype=torch.float32, device=dev)
+    ds0 = [torch.empty((B, D), dtype=torch.float32, device=dev) for _ in range(S)]
+    lam = ([torch.empty_strided((B, D, T), (ss[0], ss[1], 1), dtype=torch.float32, device=dev)
+            for _ in range(S)] if with_lambda else None)
+    shape = make_shape(B, T, D, us, ss)
+    newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
+    nws = workspace_bytes(cell, shape, newton, adjoint=True)
+    ws = workspace if workspace is not None else _ws.get(nws, dev)
+    _check(lib.pararnn_adjoint(cell, ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a),
+                               _ptr_array(s0), _ptr_array(s), _ptr_array(gs), _ptr_array(du),
+                               _ptr(da), _ptr_array(ds0),
+                               _ptr_array(lam) if lam is not None else None,
+                               ctypes.byref(newton), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream_handle(stream)))
+    return dict(du=du, da=da, ds0=ds0, lam=lam)

@@ -28,3 +28,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_case(request):
+    """Name every GPU case on stderr before it runs, so that a run that ends
+    abruptly still shows which case was on the device."""
+    if "gpu" in request.keywords:
+        sys.stderr.write(f"\n[case] {request.node.nodeid}\n")
+        sys.stderr.flush()
+    yield

@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/pararnn.h declares, plans tilings, sizes workspaces
+and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nonlinear_rnn_amd import pararnn as pr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pararnn.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pararnn_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["pararnn_solve_gru", "pararnn_solve_lstm", "pararnn_adjoint",
+              "pararnn_workspace_bytes", "pararnn_status_string", "pararnn_plan"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pr.load()
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert pr.status_string(0) == "ok"
+    for s in range(1, 5):
+        assert pr.status_string(s) != "ok"
+    assert "unknown" in pr.status_string(99)
+
+
+def test_plan_defaults():
+    # one workgroup per channel up to 4096 steps, then time blocks
+    assert pr.plan("gru", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
+    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (16, 4, 4)
+    assert pr.plan("gru", pr.make_shape(1, 1024, 64)) == (16, 1, 1)
+    assert pr.plan("gru", pr.make_shape(1, 1, 64)) == (1, 1, 1)
+    assert pr.plan("lstm", pr.make_shape(8, 4096, 1024)) == (8, 8, 1)
+    assert pr.plan("lstm", pr.make_shape(16, 2048, 4096), adjoint=True) == (8, 4, 1)
+    # forced tiling, ragged T
+    n = pr.make_newton(steps_per_lane=1, waves_per_block=1)
+    assert pr.plan("gru", pr.make_shape(2, 3 * 64 + 7, 3), n) == (1, 1, 4)
+
+
+@pytest.mark.parametrize("K,W", [(3, 1), (32, 1), (1, 16), (1, 3), (-1, 1)])
+def test_plan_rejects_unsupported_tiling(K, W):
+    n = pr.make_newton(steps_per_lane=K, waves_per_block=W)
+    with pytest.raises(pr.PararnnError) as e:
+        pr.plan("gru", pr.make_shape(1, 100, 1), n)
+    assert e.value.status == 2
+
+
+def test_workspace_sizes():
+    n = pr.make_newton(1e-6, 20)
+    assert pr.workspace_bytes("gru", pr.make_shape(8, 4096, 1024), n) == 0
+    ws = pr.workspace_bytes("gru", pr.make_shape(4, 16384, 4096), n)
+    units = 4 * 4096 * 4
+    assert ws >= units * 4 + units * 21 * 4 * 4
+    ws2 = pr.workspace_bytes("gru", pr.make_shape(4, 16384, 4096), pr.make_newton(1e-6, 20,
+                             init_from_output=True))
+    assert ws2 >= ws + units * 4
+    wl = pr.workspace_bytes("lstm", pr.make_shape(4, 16384, 4096), n)
+    assert wl > ws
+    wa = pr.workspace_bytes("lstm", pr.make_shape(16, 2048, 4096), n, adjoint=True)
+    assert wa >= 16 * 4096 * 4 * 4
+    assert pr.workspace_bytes(7, pr.make_shape(1, 1, 1), n) == 0
+
+
+def _call_gru(shape, newton, u=(1, 1, 1), a=1, h0=1, h=1, ws=None, nws=0):
+    lib = pr.load()
+    arr = (ctypes.c_void_p * 3)(*[x or None for x in u])
+    return lib.pararnn_solve_gru(ctypes.byref(shape) if shape is not None else None, arr, 0,
+                                 a, h0, h, ctypes.byref(newton) if newton else None, None,
+                                 ws, nws, None)
+
+
+def test_solve_rejects_bad_arguments_before_any_device_call():
+    good = pr.make_shape(2, 16, 3)
+    n = pr.make_newton(1e-6, 5)
+    assert _call_gru(None, n) == 1
+    assert _call_gru(good, None) == 1
+    assert _call_gru(pr.make_shape(-1, 16, 3), n) == 1
+    assert _call_gru(pr.make_shape(2, 16, 3, (48, 8)), n) == 1       # rows overlap
+    assert _call_gru(pr.make_shape(2, 16, 3, None, (-48, 16)), n) == 1
+    assert _call_gru(good, pr.make_newton(float("nan"), 5)) == 1
+    assert _call_gru(good, pr.make_newton(-1.0, 5)) == 1
+    assert _call_gru(good, pr.make_newton(float("inf"), 5)) == 1
+    assert _call_gru(good, pr.make_newton(1e-6, -1)) == 1
+    assert _call_gru(good, pr.make_newton(1e-6, 5, steps_per_lane=5)) == 2
+    assert _call_gru(good, n, u=(1, 0, 1)) == 1
+    assert _call_gru(good, n, a=None) == 1
+    assert _call_gru(good, n, h=None) == 1
+    # several time blocks need a workspace
+    nb = pr.make_newton(1e-6, 5, steps_per_lane=1, waves_per_block=1)
+    big = pr.make_shape(2, 200, 3)
+    assert _call_gru(big, nb) == 3
+    need = pr.workspace_bytes("gru", big, nb)
+    assert _call_gru(big, nb, ws=16, nws=need - 1) == 3
+    assert _call_gru(big, nb, ws=8, nws=need) == 3                     # misaligned
+
+
+def test_lstm_and_adjoint_reject_bad_arguments():
+    lib = pr.load()
+    shape = pr.make_shape(1, 8, 2)
+    n = pr.make_newton(1e-6, 5)
+    u = (ctypes.c_void_p * 4)(1, 1, 1, 1)
+    assert lib.pararnn_solve_lstm(ctypes.byref(shape), u, 0, 1, 1, None, 1, 1,
+                                  ctypes.byref(n), None, None, 0, None) == 1
+    assert lib.pararnn_solve_lstm(ctypes.byref(shape), u, 5, 1, 1, 1, 1, 1,
+                                  ctypes.byref(n), None, None, 0, None) == 2
+    s2 = (ctypes.c_void_p * 2)(1, 1)
+    assert lib.pararnn_adjoint(3, ctypes.byref(shape), u, 0, 1, s2, s2, s2, u, 1, s2, None,
+                               None, None, 0, None) == 1
+    assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, 1, s2, s2, s2, u, 1, s2, None,
+                               None, None, 0, None) == 3
+    assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, None, s2, s2, s2, u, 1, s2, None,
+                               None, None, 0, None) == 1

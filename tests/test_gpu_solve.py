@@ -1,0 +1,179 @@
+"""GPU parity of the fused Newton solve (HIP path through the C ABI) against
+the CPU oracle, plus the invariants the pages fix.
+
+Tolerances: 1e-5 max-abs for float32 states; for bf16 projections the gate is
+2e-2 against the oracle on the unrounded float32 draw, with a 1e-5
+diagnostic against the oracle on the rounded values (what the device sees).
+"""
+import numpy as np
+import pytest
+import torch
+
+from nonlinear_rnn_amd.inputs import make_inputs
+from oracle import deer
+from tests.gpu_util import gpu_solve, max_err, oracle_states
+
+pytestmark = pytest.mark.gpu
+
+TOL32 = 1e-5
+
+TILINGS = [(0, 0), (1, 1), (2, 2), (4, 1), (16, 4), (8, 8)]
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 200, 1000, 4100])
+@pytest.mark.parametrize("KW", TILINGS)
+def test_parity_small(cell, T, KW):
+    K, W = KW
+    inp = make_inputs(cell, 2, T, 3, 1000 + T, s0_std=0.1, f_bias=1.0)
+    got, info = gpu_solve(inp, 1e-6, 40, K, W)
+    ref = oracle_states(inp)
+    assert info["converged"], info
+    assert info["max_abs_res"] < 1e-6
+    assert max_err(got, ref) < TOL32
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("T,KW", [(96, (1, 1)), (1000, (1, 1)), (517, (2, 1)), (4100, (4, 4))])
+def test_parity_bf16_inputs(cell, T, KW):
+    inp = make_inputs(cell, 2, T, 5, 2000 + T, u_dtype="bf16", f_bias=1.0)
+    got, info = gpu_solve(inp, 1e-6, 40, *KW)
+    assert info["converged"]
+    assert max_err(got, oracle_states(inp, rounded=True)) < TOL32
+    assert max_err(got, oracle_states(inp, rounded=False)) < 2e-2
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("KW", [(1, 1), (2, 2), (0, 0)])
+@pytest.mark.parametrize("iters", [1, 2, 3])
+def test_per_iteration_parity_with_deer(cell, KW, iters):
+    """tol = 0 forces exactly `iters` updates everywhere; the iterate must be
+    the DEER iterate of the numpy oracle (same start s = 0)."""
+    inp = make_inputs(cell, 1, 300, 4, 3000 + iters, s0_std=0.3, f_bias=1.0)
+    got, info = gpu_solve(inp, 0.0, iters, *KW)
+    assert info["iters"] == iters and not info["converged"]
+    u = deer.from_planes(inp.u)
+    a = deer.a_per_channel(inp.a, 1)
+    s0 = np.stack([p.reshape(-1).astype(np.float64) for p in inp.s0], -1)
+    s, _ = deer.newton(cell, u, a, s0, tol=0.0, max_iters=iters)
+    ref = [s[..., c].reshape(1, 4, 300) for c in range(s.shape[-1])]
+    scale = max(1.0, max(float(np.abs(r).max()) for r in ref))
+    assert max_err(got, ref) < 1e-4 * scale
+
+
+def test_linear_gru_converges_in_one_update():
+    inp = make_inputs("gru", 2, 3000, 8, 41, s0_std=0.5)
+    inp.a[:] = 0
+    got, info = gpu_solve(inp, 1e-6, 20)
+    assert info["converged"] and info["iters"] == 1
+    assert max_err(got, oracle_states(inp)) < TOL32
+
+
+def test_linear_lstm_converges_in_two_updates():
+    inp = make_inputs("lstm", 2, 3000, 8, 42, s0_std=0.5, f_bias=1.0)
+    inp.a[:] = 0
+    got, info = gpu_solve(inp, 1e-6, 20)
+    assert info["converged"] and info["iters"] == 2
+    assert max_err(got, oracle_states(inp)) < TOL32
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_prefix_exact_after_k_updates_stiff(cell, k):
+    """After k updates from s = 0 the first k states are the exact ones, even
+    for a stiff cell (a ~ U(-4, 4))."""
+    inp = make_inputs(cell, 1, 256, 6, 50 + k, f_bias=1.0, a_scale=4.0, u_scale=2.0)
+    got, info = gpu_solve(inp, 0.0, k, 1, 1)
+    ref = oracle_states(inp)
+    assert max_err([g[..., :k] for g in got], [r[..., :k] for r in ref]) < TOL32
+
+
+@pytest.mark.parametrize("KW", [(0, 0), (1, 1)])
+def test_tol_zero_runs_to_cap(KW):
+    inp = make_inputs("gru", 1, 500, 4, 61)
+    got, info = gpu_solve(inp, 0.0, 7, *KW)
+    assert info["iters"] == 7 and not info["converged"] and not info["nan_seen"]
+    assert info["iters_sum"] == 7 * info["units"]
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("KW", [(0, 0), (1, 1)])
+def test_nan_input_is_reported(cell, KW):
+    inp = make_inputs(cell, 2, 400, 3, 71, f_bias=1.0)
+    inp.u[0][1, 2, 123] = np.nan
+    got, info = gpu_solve(inp, 1e-6, 10, *KW)
+    assert info["nan_seen"] and not info["converged"]
+    assert np.isnan(info["max_abs_res"])
+    ref = oracle_states(inp)
+    # every other channel is unaffected
+    for g, r in zip(got, ref):
+        g, r = g.copy(), r.copy()
+        g[1, 2] = 0
+        r[1, 2] = 0
+        assert np.max(np.abs(g - r)) < TOL32
+    assert np.isnan(got[-1][1, 2, 123:]).all()
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_bitwise_deterministic(cell):
+    inp = make_inputs(cell, 2, 5000, 16, 81, f_bias=1.0)
+    a, ia = gpu_solve(inp, 1e-6, 20, 2, 2)
+    b, ib = gpu_solve(inp, 1e-6, 20, 2, 2)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert ia == ib
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("KW", [(0, 0), (1, 1)])
+def test_warm_start(cell, KW):
+    inp = make_inputs(cell, 2, 700, 4, 91, s0_std=0.2, f_bias=1.0)
+    ref = oracle_states(inp)
+    start = [r.astype(np.float32) for r in ref]
+    got, info = gpu_solve(inp, 1e-6, 20, *KW, init=start)
+    assert info["iters"] == 0 and info["converged"]
+    for g, s in zip(got, start):
+        assert np.array_equal(g, s)
+    # a perturbed start converges to the same trajectory
+    rng = np.random.default_rng(5)
+    pert = [s + rng.standard_normal(s.shape).astype(np.float32) * 0.05 for s in start]
+    got, info = gpu_solve(inp, 1e-6, 20, *KW, init=pert)
+    assert info["converged"] and info["iters"] >= 1
+    assert max_err(got, ref) < TOL32
+
+
+def test_empty_problems():
+    for B, T, D in [(0, 10, 3), (2, 0, 3), (2, 10, 0)]:
+        inp = make_inputs("gru", B, T, D, 1)
+        got, info = gpu_solve(inp, 1e-6, 5)
+        assert got[0].shape == (B, D, T)
+        assert info["converged"] and info["iters"] == 0
+
+
+def test_strided_planes():
+    """Planes that are views of larger buffers (row strides > T, not 16-byte
+    multiples) take the scalar load path and give the same answer."""
+    from nonlinear_rnn_amd import pararnn as pr
+    inp = make_inputs("gru", 2, 301, 3, 97, s0_std=0.1)
+    ref = oracle_states(inp)
+    big = [torch.zeros((2, 3, 307), device="cuda") for _ in range(3)]
+    for g in range(3):
+        big[g][:, :, 2:303] = torch.from_numpy(inp.u[g]).cuda()
+    u = [x[:, :, 2:303] for x in big]
+    out_big = torch.zeros((2, 3, 305), device="cuda")
+    out = out_big[:, :, 1:302]
+    h, info = pr.solve_gru(u, torch.from_numpy(inp.a).cuda(), torch.from_numpy(inp.s0[0]).cuda(),
+                           out=out, tol=1e-6, max_iters=20)
+    assert pr.read_info(info)["converged"]
+    assert max_err([out.cpu().numpy()], ref) < TOL32
+    assert float(out_big[:, :, 0].abs().max()) == 0.0
+    assert float(out_big[:, :, 302:].abs().max()) == 0.0
+
+
+def test_runs_on_a_side_stream():
+    inp = make_inputs("lstm", 2, 1500, 5, 99, f_bias=1.0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got, info = gpu_solve(inp, 1e-6, 20, stream=s)
+    assert info["converged"]
+    assert max_err(got, oracle_states(inp)) < TOL32
