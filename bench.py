@@ -76,11 +76,16 @@ def cpu_baseline(w, inp, budget_s=12.0):
     dt = run(n)
     target = int(n * budget_s / max(dt, 1e-3))
     n = max(n, min(w.B * w.D, target))
-    dt = run(n)
+    # repeat the sample until about budget_s of CPU time (core-seconds) is spent
+    reps, total = 0, 0.0
+    while reps == 0 or total * threads < budget_s:
+        total += run(n)
+        reps += 1
+    dt = total / reps
     elems = n * w.T
     return {"value": elems / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {w.B * w.D} channels x T={w.T} (fp64 sequential, "
-                      f"OpenMP over channels), {dt:.2f} s"}
+            "sample": f"{n} of {w.B * w.D} channels x T={w.T} (fp64 sequential step-by-step, "
+                      f"OpenMP over channels), mean of {reps} runs, {dt:.3f} s each"}
 
 
 def main():
@@ -90,6 +95,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gru_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, copy a buffer of this many MiB three "
+                         "times (plain device copy used to calibrate HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
@@ -174,6 +182,14 @@ def main():
                      "kernel": "newton_kernel", "kernel_ms_avg": kavg_ms,
                      "kernel_ms_min": kmin_ms},
     }
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n * 4
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)

@@ -260,15 +260,14 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
     if (A.nb > 1) {
         if (threadIdx.x == 0) {
             rec_store(A.records + unit * RF, blk, 0u);
-            store_release(A.flags + unit, 1);
+            publish_flag(A.flags + unit, 1);
         }
         if (k < A.nb - 1) {
             const int32_t *flags = A.flags + ch * A.nb;
             for (int32_t j = k + 1; j < A.nb; ++j) {
-                while (__hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 1)
-                    __builtin_amdgcn_s_sleep(2);
+                while (load_flag(flags + j) < 1) __builtin_amdgcn_s_sleep(2);
             }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            after_flag();
             for (int32_t j = A.nb - 1; j > k; --j) {
                 M mj;
                 rec_load(A.records + (ch * A.nb + j) * RF, mj);

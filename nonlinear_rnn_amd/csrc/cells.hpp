@@ -47,9 +47,9 @@ struct GruCell {
     static __device__ __forceinline__ float uscale(int g) { return g == 2 ? -2.0f * kLog2e : -kLog2e; }
 
     // Affine map of one step at (h_{t-1} = hp, u_t) for the current iterate
-    // h_t = h; folds |r_t| into mx.
+    // h_t = h.  b = -r_t.
     static __device__ __forceinline__ Map1 step_map(const Coef &p, const float (&u)[G],
-                                                    const Vec1 &hp_, const Vec1 &h_, uint32_t &mx)
+                                                    const Vec1 &hp_, const Vec1 &h_)
     {
         const float hp = hp_.x;
         const float z = sigmoid_q(fmaf_(p.qz, hp, u[0]));
@@ -57,15 +57,11 @@ struct GruCell {
         const float rh = r * hp;
         const float c = tanh_q(fmaf_(p.qc, rh, u[2]));
         const float cmh = c - hp;
-        const float f = fmaf_(z, cmh, hp);          // (1 - z) h + z c
-        const float b = f - h_.x;                   // -r_t
-        mx = max(mx, absbits(b));
-        // df/dh = (1 - z) + (c - h) z(1 - z) a_z + z (1 - c^2) a_c (r + h r(1 - r) a_r)
+        const float b = fmaf_(z, cmh, hp - h_.x);   // f - h_t = -r_t, f = (1 - z) h + z c
+        // df/dh = (1 - z) + z [ (c - h)(1 - z) a_z + (1 - c^2) a_c r (1 + h (1 - r) a_r) ]
         const float omz = 1.0f - z;
-        const float dz = (z * omz) * p.az;
-        const float dr = (r * (1.0f - r)) * p.ar;
-        const float dc = fmaf_(-c, c, 1.0f) * p.ac * fmaf_(hp, dr, r);
-        const float J = fmaf_(cmh, dz, fmaf_(z, dc, omz));
+        const float dcr = fmaf_(-c, c, 1.0f) * p.ac * (r * fmaf_(hp * (1.0f - r), p.ar, 1.0f));
+        const float J = fmaf_(z, fmaf_(cmh * omz, p.az, dcr), omz);
         return {J, b};
     }
 };
@@ -96,7 +92,7 @@ struct LstmCell {
     static __device__ __forceinline__ float uscale(int g) { return g == 2 ? -2.0f * kLog2e : -kLog2e; }
 
     static __device__ __forceinline__ Map2 step_map(const Coef &p, const float (&u)[G],
-                                                    const Vec2 &sp, const Vec2 &s, uint32_t &mx)
+                                                    const Vec2 &sp, const Vec2 &s)
     {
         const float cp = sp.x0, hp = sp.x1;
         const float i = sigmoid_q(fmaf_(p.qi, hp, u[0]));
@@ -109,7 +105,6 @@ struct LstmCell {
         Map2 m;
         m.b0 = c - s.x0;
         m.b1 = h - s.x1;
-        mx = max(mx, max(absbits(m.b0), absbits(m.b1)));
         // dc'/dc = f
         // dc'/dh = c f(1-f) a_f + g i(1-i) a_i + i (1-g^2) a_g
         // dh'/dc = o (1 - tanh^2 c') f

@@ -38,6 +38,7 @@ int rec_floats(pararnn_cell_t c) { return c == PARARNN_LSTM ? MapRec<Map2>::kFlo
 bool rows_disjoint(int64_t B, int64_t T, int64_t D, int64_t sb, int64_t sd)
 {
     if (sb < 0 || sd < 0) return false;
+    if (B == 0 || D == 0 || T == 0) return true;  // no elements
     if (B <= 1 && D <= 1) return true;
     if (B <= 1) return sd >= T;
     if (D <= 1) return sb >= T;

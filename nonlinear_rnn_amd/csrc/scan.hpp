@@ -55,6 +55,13 @@ __device__ __forceinline__ Map1 compose(const Map1 &L, const Map1 &E)
 struct Vec1 {
     float x;
 };
+// max |b| of a map's residual part, as unsigned bits (see absbits)
+__device__ __forceinline__ uint32_t resbits(const Map1 &m) { return absbits(m.b); }
+// the identity where `keep` is false (select, no branch)
+__device__ __forceinline__ Map1 keep_or_identity(const Map1 &m, bool keep)
+{
+    return {keep ? m.a : 1.0f, keep ? m.b : 0.0f};
+}
 __device__ __forceinline__ Vec1 apply(const Map1 &m, const Vec1 &v) { return {fmaf_(m.a, v.x, m.b)}; }
 
 struct Map2 {  // 2x2 block Jacobian (ParaLSTM), state order (c, h)
@@ -75,6 +82,12 @@ __device__ __forceinline__ Map2 compose(const Map2 &L, const Map2 &E)
 struct Vec2 {
     float x0, x1;
 };
+__device__ __forceinline__ uint32_t resbits(const Map2 &m) { return max(absbits(m.b0), absbits(m.b1)); }
+__device__ __forceinline__ Map2 keep_or_identity(const Map2 &m, bool keep)
+{
+    return {keep ? m.a00 : 1.0f, keep ? m.a01 : 0.0f, keep ? m.a10 : 0.0f,
+            keep ? m.a11 : 1.0f, keep ? m.b0 : 0.0f,  keep ? m.b1 : 0.0f};
+}
 __device__ __forceinline__ Vec2 apply(const Map2 &m, const Vec2 &v)
 {
     return {fmaf_(m.a00, v.x0, fmaf_(m.a01, v.x1, m.b0)),
@@ -158,16 +171,11 @@ __device__ __forceinline__ float wave_sum_to_last(float x)
 }
 
 // ------------------------------------------------ device-scope flag ops ---
-__device__ __forceinline__ int32_t load_acquire(const int32_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_release(int32_t *p, int32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Payload words next to a flag are read with device-coherent relaxed loads
-// (vector memory, never the scalar cache) after an acquire on the flag.
+// Cross-workgroup records are written and read only with device-coherent
+// (agent-scope) atomic accesses, which go to the coherence point themselves;
+// so publishing needs no cache maintenance, only ordering.  A release/acquire
+// fence at agent scope would write back / invalidate the XCD's whole L2 on
+// every publish, which costs far more than the exchange itself.
 __device__ __forceinline__ float load_relaxed(const float *p)
 {
     return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p),
@@ -178,5 +186,20 @@ __device__ __forceinline__ void store_relaxed(float *p, float v)
     __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int32_t load_flag(const int32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Flag store ordered after every earlier store of this lane: wait until those
+// have completed (reached the coherence point), then write the flag.
+__device__ __forceinline__ void publish_flag(int32_t *p, int32_t v)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// After a flag read has returned the awaited value: keep the compiler from
+// hoisting the payload loads above it (the hardware issues them after the
+// flag value was consumed by the branch).
+__device__ __forceinline__ void after_flag() { asm volatile("" ::: "memory"); }
 
 }  // namespace pararnn

@@ -218,17 +218,17 @@ __device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_
     // record of this iteration.
     int32_t start = 0;
     for (int32_t j = k - 1; j >= 0; --j) {
-        int32_t v = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int32_t v = load_flag(flags + j);
         while (v < it + 1) {
             __builtin_amdgcn_s_sleep(2);
-            v = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v = load_flag(flags + j);
         }
         if (v >= kStopBase && v - kStopBase <= it) {
             start = j + 1;
             break;
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    after_flag();
     // Pass 2: blocks start..p-1 all report |r| < tol at `it`, so they stop
     // now (their carry-out is zero); the carry is the fold of p..k-1.
     int32_t p = start;
@@ -280,6 +280,7 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
     const int64_t tb0 = (int64_t)k * P;
     const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
     const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
+    const bool full = tb0 + P <= T;  // uniform over the workgroup
 
     const typename Cell::Coef cf = Cell::coef(A.a, A.D, d);
 
@@ -332,22 +333,34 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
     }
 
     const uint32_t tolb = __float_as_uint(A.tol);
-    M m[K];
+    M m[K];  // running composition of the lane's steps 0..kk
     int32_t it = 0;
     uint32_t bmx = 0;
     for (;; ++it) {
-        // ---- residual, Jacobian and lane up-sweep
+        // ---- residual, Jacobian and lane up-sweep.  Blocks that lie wholly
+        // inside [0, T) take a path without per-step masks; the ragged last
+        // block turns steps past T into identity maps by selection.
         uint32_t mx = 0;
         M agg = identity_map(M{});
         V prev = hin;
+        if (full) {
 #pragma unroll
-        for (int kk = 0; kk < K; ++kk) {
-            if (t0 + kk < T)
-                m[kk] = Cell::step_map(cf, u[kk], prev, s[kk], mx);
-            else
-                m[kk] = identity_map(M{});
-            prev = s[kk];
-            agg = kk == 0 ? m[0] : compose(m[kk], agg);
+            for (int kk = 0; kk < K; ++kk) {
+                const M mk = Cell::step_map(cf, u[kk], prev, s[kk]);
+                mx = max(mx, resbits(mk));
+                prev = s[kk];
+                agg = kk == 0 ? mk : compose(mk, agg);
+                m[kk] = agg;
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) {
+                const M mk = keep_or_identity(Cell::step_map(cf, u[kk], prev, s[kk]), t0 + kk < T);
+                mx = max(mx, resbits(mk));
+                prev = s[kk];
+                agg = kk == 0 ? mk : compose(mk, agg);
+                m[kk] = agg;
+            }
         }
         // ---- wave scan, then block exchange through LDS
         const M inc = wave_scan_inclusive(agg);
@@ -370,14 +383,14 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
         const bool at_cap = (it == A.cap);
         if (A.nb > 1 && threadIdx.x == 0) {
             rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
-            store_release(A.flags + unit, it + 1);
+            publish_flag(A.flags + unit, it + 1);
         }
         if (at_cap) break;
         V din = vzero<V>();
         bool pred_stopped = true;
         if (k > 0) look_back<M, V>(A, ch, k, it, din, pred_stopped);
         if (cbit && pred_stopped) {
-            if (A.nb > 1 && threadIdx.x == 0) store_release(A.flags + unit, kStopBase + it);
+            if (A.nb > 1 && threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
             break;
         }
         // ---- down-sweep from the carries, Newton update
@@ -388,12 +401,11 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
         const V dl = apply(exc, dw);
         const V dout = (A.nb > 1 && last_lane_of_block) ? apply(blk, din) : apply(inc, dw);
         hin = vadd(hin, dl);
-        V dd = dl;
+        // m[kk] holds the lane's running composition of steps 0..kk, so every
+        // step's correction comes straight from the lane carry-in (no serial
+        // chain); the last step takes the carry the next lane also sees.
 #pragma unroll
-        for (int kk = 0; kk < K - 1; ++kk) {
-            dd = apply(m[kk], dd);
-            s[kk] = vadd(s[kk], dd);
-        }
+        for (int kk = 0; kk < K - 1; ++kk) s[kk] = vadd(s[kk], apply(m[kk], dl));
         s[K - 1] = vadd(s[K - 1], dout);
     }
 

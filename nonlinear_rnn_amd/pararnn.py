@@ -117,6 +117,7 @@ def _strides(planes, name):
 
 
 def make_shape(B, T, D, u_strides=None, s_strides=None):
+    """Shape record; strides default to dense [B][D][T]."""
     us = u_strides or (D * T, T)
     ss = s_strides or (D * T, T)
     return Shape(B, T, D, us[0], us[1], ss[0], ss[1])
@@ -253,8 +254,8 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
         raise ValueError("wrong number of gate or state planes")
     B, D, T = u[0].shape
     dev = u[0].device
-    us = _strides(u, "u")
-    ss = _strides(s + [g for g in gs if g is not None], "states")
+    us = _strides(u, "u") or (D * T, T)
+    ss = _strides(s + [g for g in gs if g is not None], "states") or (D * T, T)
     du = [torch.empty_strided((B, D, T), (us[0], us[1], 1), dtype=torch.float32, device=dev)
           for _ in range(G)]
     da = torch.empty((G, D), dtype=torch.float32, device=dev)
