@@ -1,7 +1,9 @@
 """Build libpararnn.so (HIP, gfx950) in-tree.
 
-``python -m nonlinear_rnn_amd.build`` compiles ``csrc/pararnn.hip`` with
-hipcc into ``nonlinear_rnn_amd/libpararnn.so``.  Packed FP32 instruction
+``python -m nonlinear_rnn_amd.build`` compiles the host ABI
+(``csrc/pararnn.hip``) and the kernel instantiations (``csrc/inst_*.hip``,
+one per cell and projection dtype, compiled in parallel) with hipcc and links
+``nonlinear_rnn_amd/libpararnn.so``.  Packed FP32 instruction
 selection is switched off for the device code; every kernel is written for
 wave64 CDNA4 and needs no other target.
 """
@@ -9,6 +11,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -31,19 +34,38 @@ def compile_flags():
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(CSRC, "pararnn.hip")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + compile_flags() + ["-shared", src, "-o", tmp]
+SOURCES = ["pararnn.hip", "inst_gru_f32.hip", "inst_gru_bf16.hip", "inst_lstm_f32.hip",
+           "inst_lstm_bf16.hip"]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines()
                     if "is not a recognized feature for this target" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every translation unit (in parallel) and link the library."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cc = hipcc()
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([cc] + compile_flags() + ["-c", os.path.join(CSRC, src), "-o", obj])
+    jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -263,15 +263,22 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
             publish_flag(A.flags + unit, 1);
         }
         if (k < A.nb - 1) {
+            // later blocks k+1..nb-1, one per lane, folded from the last one
+            const int lane = threadIdx.x & (kWave - 1);
             const int32_t *flags = A.flags + ch * A.nb;
-            for (int32_t j = k + 1; j < A.nb; ++j) {
-                while (load_flag(flags + j) < 1) __builtin_amdgcn_s_sleep(2);
-            }
-            after_flag();
-            for (int32_t j = A.nb - 1; j > k; --j) {
-                M mj;
-                rec_load(A.records + (ch * A.nb + j) * RF, mj);
-                din = apply(mj, din);
+            for (int32_t hi = A.nb; hi > k + 1; hi -= kWave) {
+                const int32_t lo = hi - kWave > k + 1 ? hi - kWave : k + 1;
+                const int32_t j = lo + lane;
+                const bool mine = j < hi;
+                int32_t v = mine ? load_flag(flags + j) : 1;
+                while (!__all(!mine || v >= 1)) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (mine && v < 1) v = load_flag(flags + j);
+                }
+                after_flag();
+                M mj = identity_map(M{});
+                if (mine) rec_load(A.records + (ch * A.nb + j) * RF, mj);
+                for (int32_t q = hi - lo - 1; q >= 0; --q) din = apply(readlane_map(mj, q), din);
             }
         }
     }
@@ -328,6 +335,7 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
     }
 }
 
+#ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit
 __global__ void adjoint_init_kernel(AdjArgs A, int32_t S, int32_t G, int64_t units)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -356,5 +364,7 @@ __global__ void da_reduce_kernel(AdjArgs A, int32_t G)
         for (int32_t k = 0; k < A.nb; ++k) acc += A.da_part[((b * A.D + d) * A.nb + k) * G + g];
     A.da[i] = acc;
 }
+
+#endif
 
 }  // namespace pararnn

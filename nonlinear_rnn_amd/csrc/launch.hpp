@@ -1,0 +1,83 @@
+// Kernel launchers, one set per (cell, projection dtype); each set is
+// instantiated in its own translation unit (inst_*.hip) so the tiling
+// variants compile in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "adjoint.hpp"
+#include "solve.hpp"
+
+namespace pararnn {
+
+// Tilings with kernels: steps per lane K and waves per workgroup W.
+inline bool newton_tiling_built(bool lstm, int K, int W)
+{
+    const bool base = (K == 1 || K == 2 || K == 4 || K == 8 || K == 16) &&
+                      (W == 1 || W == 2 || W == 4 || W == 8);
+    return base || (!lstm && K == 32 && (W == 1 || W == 2));
+}
+inline bool adjoint_tiling_built(bool, int K, int W)
+{
+    return (K == 1 || K == 2 || K == 4 || K == 8 || K == 16) &&
+           (W == 1 || W == 2 || W == 4 || W == 8);
+}
+
+#define PARARNN_DECLARE_LAUNCHERS(NAME)                                                          \
+    hipError_t launch_newton_##NAME(int K, int W, bool full, int64_t groups, hipStream_t st,    \
+                                    const SolveArgs &a);                                        \
+    hipError_t launch_adjoint_##NAME(int K, int W, int64_t groups, hipStream_t st,              \
+                                     const AdjArgs &a);
+PARARNN_DECLARE_LAUNCHERS(gru_f32)
+PARARNN_DECLARE_LAUNCHERS(gru_bf16)
+PARARNN_DECLARE_LAUNCHERS(lstm_f32)
+PARARNN_DECLARE_LAUNCHERS(lstm_bf16)
+#undef PARARNN_DECLARE_LAUNCHERS
+
+#define PARARNN_BASE_KW(X)                                                                      \
+    X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 1) X(4, 2) X(4, 4)    \
+        X(4, 8) X(8, 1) X(8, 2) X(8, 4) X(8, 8) X(16, 1) X(16, 2) X(16, 4) X(16, 8)
+
+#define PARARNN_NEWTON_CASE(CELL, BF16, KK, WW)                                                 \
+    case KK * 100 + WW:                                                                         \
+        if (full)                                                                               \
+            hipLaunchKernelGGL((newton_kernel<CELL, KK, WW, BF16, true>), grid, block, 0, st, a); \
+        else                                                                                    \
+            hipLaunchKernelGGL((newton_kernel<CELL, KK, WW, BF16, false>), grid, block, 0, st, a); \
+        break;
+
+#define PARARNN_ADJOINT_CASE(CELL, BF16, KK, WW)                                                \
+    case KK * 100 + WW:                                                                         \
+        hipLaunchKernelGGL((adjoint_kernel<CELL, KK, WW, BF16>), grid, block, 0, st, a);        \
+        break;
+
+// EXTRA(X) lists tilings beyond the base set for this cell.
+#define PARARNN_DEFINE_LAUNCHERS(NAME, CELL, BF16, EXTRA)                                       \
+    hipError_t launch_newton_##NAME(int K, int W, bool full, int64_t groups, hipStream_t st,    \
+                                    const SolveArgs &a)                                         \
+    {                                                                                           \
+        const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
+        switch (K * 100 + W) {                                                                  \
+            PARARNN_BASE_KW(PARARNN_NEWTON_CASE_##NAME)                                         \
+            EXTRA(PARARNN_NEWTON_CASE_##NAME)                                                   \
+        default:                                                                                \
+            return hipErrorInvalidValue;                                                        \
+        }                                                                                       \
+        return hipGetLastError();                                                               \
+    }                                                                                           \
+    hipError_t launch_adjoint_##NAME(int K, int W, int64_t groups, hipStream_t st,              \
+                                     const AdjArgs &a)                                          \
+    {                                                                                           \
+        const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
+        switch (K * 100 + W) {                                                                  \
+            PARARNN_BASE_KW(PARARNN_ADJOINT_CASE_##NAME)                                        \
+        default:                                                                                \
+            return hipErrorInvalidValue;                                                        \
+        }                                                                                       \
+        return hipGetLastError();                                                               \
+    }
+
+#define PARARNN_NO_EXTRA(X)
+#define PARARNN_GRU_EXTRA(X) X(32, 1) X(32, 2)
+
+}  // namespace pararnn

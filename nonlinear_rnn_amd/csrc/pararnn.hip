@@ -8,9 +8,9 @@
 #include <cstdint>
 #include <cstring>
 
-#include "adjoint.hpp"
+#define PARARNN_DEFINE_AUX_KERNELS
+#include "launch.hpp"
 #include "pararnn.h"
-#include "solve.hpp"
 
 using namespace pararnn;
 
@@ -56,6 +56,11 @@ pararnn_status_t check_shape(const pararnn_shape_t *sh)
     return PARARNN_OK;
 }
 
+bool opt_k_w_unset(const pararnn_newton_t *opt)
+{
+    return !opt || (opt->steps_per_lane == 0 && opt->waves_per_block == 0);
+}
+
 // Default tiling: the smallest block capacity P = 64 W K that covers T, from
 // a list ordered by preference; past the largest one, several time blocks
 // per channel.
@@ -66,11 +71,11 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
     if (st != PARARNN_OK) return st;
     int K = opt ? opt->steps_per_lane : 0;
     int W = opt ? opt->waves_per_block : 0;
-    if ((K != 0 && !pow2_in(K, 1, 16)) || (W != 0 && !pow2_in(W, 1, 8)))
+    if ((K != 0 && !pow2_in(K, 1, 32)) || (W != 0 && !pow2_in(W, 1, 8)))
         return PARARNN_ERR_UNSUPPORTED;
     if (K == 0 || W == 0) {
         static const int gru_kw[][2] = {{16, 4}, {16, 2}, {16, 1}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
-        static const int lstm_kw[][2] = {{8, 8}, {8, 4}, {8, 2}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
+        static const int lstm_kw[][2] = {{16, 4}, {16, 2}, {16, 1}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
         static const int adj_kw[][2] = {{8, 4}, {8, 2}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
         const int(*tab)[2] = adjoint ? adj_kw : (cell == PARARNN_LSTM ? lstm_kw : gru_kw);
         const int n = adjoint ? 6 : 7;
@@ -81,7 +86,18 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
         }
         if (K == 0) K = tab[pick][0];
         if (W == 0) W = tab[pick][1];
+        // Past one workgroup per channel, GRU time blocks of 2 waves x 32
+        // steps per lane (the same 4096 steps) need half the cross-block
+        // exchanges per step of the 4-wave layout.
+        if (!adjoint && cell == PARARNN_GRU && opt_k_w_unset(opt) &&
+            sh->T > (int64_t)kWave * tab[0][0] * tab[0][1]) {
+            K = 32;
+            W = 2;
+        }
     }
+    const bool lstm = cell == PARARNN_LSTM;
+    if (adjoint ? !adjoint_tiling_built(lstm, K, W) : !newton_tiling_built(lstm, K, W))
+        return PARARNN_ERR_UNSUPPORTED;
     pl.K = K;
     pl.W = W;
     pl.P = (int64_t)kWave * K * W;
@@ -128,27 +144,6 @@ pararnn_status_t check_newton(const pararnn_newton_t *opt)
     if (opt->max_iters < 0 || opt->max_iters > kMaxIters) return PARARNN_ERR_INVALID;
     if (opt->init_from_output != 0 && opt->init_from_output != 1) return PARARNN_ERR_INVALID;
     return PARARNN_OK;
-}
-
-#define PARARNN_KW_CASES(X)                                                                 \
-    X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 1) X(4, 2) X(4, 4)  \
-        X(4, 8) X(8, 1) X(8, 2) X(8, 4) X(8, 8) X(16, 1) X(16, 2) X(16, 4) X(16, 8)
-
-template <class Cell, bool BF16>
-hipError_t launch_newton(int K, int W, int64_t groups, hipStream_t st, const SolveArgs &a)
-{
-    const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));
-    switch (K * 100 + W) {
-#define X(KK, WW)                                                                           \
-    case KK * 100 + WW:                                                                     \
-        hipLaunchKernelGGL((newton_kernel<Cell, KK, WW, BF16>), grid, block, 0, st, a);     \
-        break;
-        PARARNN_KW_CASES(X)
-#undef X
-    default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, const void *const *u,
@@ -223,13 +218,14 @@ pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, co
     }
     if (!work) return PARARNN_OK;
     const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+    const bool full = sh->T % pl.P == 0;
     hipError_t e;
     if (cell == PARARNN_GRU)
-        e = dt == PARARNN_BF16 ? launch_newton<GruCell, true>(pl.K, pl.W, groups, strm, A)
-                               : launch_newton<GruCell, false>(pl.K, pl.W, groups, strm, A);
+        e = dt == PARARNN_BF16 ? launch_newton_gru_bf16(pl.K, pl.W, full, groups, strm, A)
+                               : launch_newton_gru_f32(pl.K, pl.W, full, groups, strm, A);
     else
-        e = dt == PARARNN_BF16 ? launch_newton<LstmCell, true>(pl.K, pl.W, groups, strm, A)
-                               : launch_newton<LstmCell, false>(pl.K, pl.W, groups, strm, A);
+        e = dt == PARARNN_BF16 ? launch_newton_lstm_bf16(pl.K, pl.W, full, groups, strm, A)
+                               : launch_newton_lstm_f32(pl.K, pl.W, full, groups, strm, A);
     return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
 }
 
@@ -253,23 +249,6 @@ AdjWs adj_ws_layout(pararnn_cell_t cell, const Plan &pl)
     off = align_up(off + (size_t)pl.units * cell_G(cell) * sizeof(float));
     w.total = off;
     return w;
-}
-
-template <class Cell, bool BF16>
-hipError_t launch_adjoint(int K, int W, int64_t groups, hipStream_t st, const AdjArgs &a)
-{
-    const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));
-    switch (K * 100 + W) {
-#define X(KK, WW)                                                                           \
-    case KK * 100 + WW:                                                                     \
-        hipLaunchKernelGGL((adjoint_kernel<Cell, KK, WW, BF16>), grid, block, 0, st, a);    \
-        break;
-        PARARNN_KW_CASES(X)
-#undef X
-    default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -421,11 +400,11 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
         const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
         hipError_t e;
         if (cell == PARARNN_GRU)
-            e = u_dtype == PARARNN_BF16 ? launch_adjoint<GruCell, true>(pl.K, pl.W, groups, strm, A)
-                                        : launch_adjoint<GruCell, false>(pl.K, pl.W, groups, strm, A);
+            e = u_dtype == PARARNN_BF16 ? launch_adjoint_gru_bf16(pl.K, pl.W, groups, strm, A)
+                                        : launch_adjoint_gru_f32(pl.K, pl.W, groups, strm, A);
         else
-            e = u_dtype == PARARNN_BF16 ? launch_adjoint<LstmCell, true>(pl.K, pl.W, groups, strm, A)
-                                        : launch_adjoint<LstmCell, false>(pl.K, pl.W, groups, strm, A);
+            e = u_dtype == PARARNN_BF16 ? launch_adjoint_lstm_bf16(pl.K, pl.W, groups, strm, A)
+                                        : launch_adjoint_lstm_f32(pl.K, pl.W, groups, strm, A);
         if (e != hipSuccess) return PARARNN_ERR_HIP;
     }
     {

@@ -202,43 +202,77 @@ __device__ __forceinline__ void ticket_to_unit(int64_t t, int32_t nb, int64_t &c
     ch = g * 8 + (r & 7);
 }
 
+// Map held by lane `src` of the wave, read by every lane (wave-uniform).
+__device__ __forceinline__ float readlane_f(float x, int src)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+__device__ __forceinline__ Map1 readlane_map(const Map1 &m, int src)
+{
+    return {readlane_f(m.a, src), readlane_f(m.b, src)};
+}
+__device__ __forceinline__ Map2 readlane_map(const Map2 &m, int src)
+{
+    return {readlane_f(m.a00, src), readlane_f(m.a01, src), readlane_f(m.a10, src),
+            readlane_f(m.a11, src), readlane_f(m.b0, src),  readlane_f(m.b1, src)};
+}
+
 // Look-back for time block k of channel `ch` at Newton iteration `it`:
 // returns the carry ds at the step before the block, and whether every
-// earlier block has stopped by `it`.
+// earlier block has stopped by `it`.  Lane j of the wave handles predecessor
+// lo + j, so a window of up to 64 predecessors costs one flag load and one
+// record load per lane instead of a chain of dependent loads.
 template <class M, class V>
 __device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_t k, int32_t it,
                                           V &din, bool &pred_stopped)
 {
     constexpr int RF = MapRec<M>::kFloats;
+    const int lane = threadIdx.x & (kWave - 1);
     const int32_t *flags = A.flags + ch * A.nb;
     const float *rec = A.records + (ch * A.nb) * (int64_t)(A.cap + 1) * RF;
     const int64_t rstride = (int64_t)(A.cap + 1) * RF;
-    // Pass 1: walk back to the nearest block that stopped at or before `it`
-    // (every block before it stopped no later), waiting for each one's
-    // record of this iteration.
+    // Pass 1: from k-1 downwards, find the nearest block that stopped at or
+    // before `it` (every block before it stopped no later); wait until each
+    // block above it has published its record of this iteration.
     int32_t start = 0;
-    for (int32_t j = k - 1; j >= 0; --j) {
-        int32_t v = load_flag(flags + j);
-        while (v < it + 1) {
-            __builtin_amdgcn_s_sleep(2);
-            v = load_flag(flags + j);
+    for (int32_t hi = k; hi > 0; hi -= kWave) {
+        const int32_t lo = hi > kWave ? hi - kWave : 0;
+        const int32_t j = lo + lane;
+        const bool mine = j < hi;
+        int32_t v = mine ? load_flag(flags + j) : kStopBase;
+        while (!__all(!mine || v >= it + 1)) {
+            __builtin_amdgcn_s_sleep(1);
+            if (mine && v < it + 1) v = load_flag(flags + j);
         }
-        if (v >= kStopBase && v - kStopBase <= it) {
-            start = j + 1;
+        const unsigned long long stopped =
+            __ballot(mine && v >= kStopBase && v - kStopBase <= it);
+        if (stopped) {
+            start = lo + (63 - __clzll(stopped)) + 1;
             break;
         }
     }
     after_flag();
     // Pass 2: blocks start..p-1 all report |r| < tol at `it`, so they stop
-    // now (their carry-out is zero); the carry is the fold of p..k-1.
-    int32_t p = start;
-    while (p < k && rec_cbit(rec + p * rstride + it * RF, RF)) ++p;
+    // now (their carry-out is zero); the carry is the ordered fold of p..k-1.
+    int32_t p = k;
+    for (int32_t lo = start; lo < k; lo += kWave) {
+        const int32_t j = lo + lane;
+        const bool mine = j < k;
+        const uint32_t cb = mine ? rec_cbit(rec + j * rstride + it * RF, RF) : 1u;
+        const unsigned long long open = __ballot(mine && cb == 0u);
+        if (open) {
+            p = lo + __ffsll((long long)open) - 1;
+            break;
+        }
+    }
     pred_stopped = (p == k);
     din = vzero<V>();
-    for (int32_t j = p; j < k; ++j) {
-        M m;
-        rec_load(rec + j * rstride + it * RF, m);
-        din = apply(m, din);
+    for (int32_t lo = p; lo < k; lo += kWave) {
+        const int32_t j = lo + lane;
+        M mj = identity_map(M{});
+        if (j < k) rec_load(rec + j * rstride + it * RF, mj);
+        const int32_t n = (k - lo) < kWave ? (k - lo) : kWave;
+        for (int32_t q = 0; q < n; ++q) din = apply(readlane_map(mj, q), din);
     }
 }
 
@@ -248,7 +282,10 @@ struct Slot {
     uint32_t mx;
 };
 
-template <class Cell, int K, int W, bool BF16>
+// FULL: every time block lies wholly inside [0, T) (T a multiple of the
+// block capacity), so the hot loop carries no per-step masks at all; the
+// other variant turns steps past T into identity maps by selection.
+template <class Cell, int K, int W, bool BF16, bool FULL>
 __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
 {
     using M = typename Cell::Map;
@@ -280,7 +317,7 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
     const int64_t tb0 = (int64_t)k * P;
     const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
     const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
-    const bool full = tb0 + P <= T;  // uniform over the workgroup
+    const bool full = FULL || tb0 + P <= T;  // uniform over the workgroup
 
     const typename Cell::Coef cf = Cell::coef(A.a, A.D, d);
 
@@ -428,6 +465,7 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
     }
 }
 
+#ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit
 // Clears the per-launch state (ticket counter, block flags, info record) and
 // gathers the initial boundary states a warm-started multi-block solve needs.
 __global__ void solve_init_kernel(SolveArgs A, int32_t S, int64_t units, int32_t P)
@@ -455,5 +493,7 @@ __global__ void solve_init_kernel(SolveArgs A, int32_t S, int64_t units, int32_t
         }
     }
 }
+
+#endif
 
 }  // namespace pararnn

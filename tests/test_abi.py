@@ -42,22 +42,32 @@ def test_status_strings():
 def test_plan_defaults():
     # one workgroup per channel up to 4096 steps, then time blocks
     assert pr.plan("gru", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
-    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (16, 4, 4)
+    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (32, 2, 4)
     assert pr.plan("gru", pr.make_shape(1, 1024, 64)) == (16, 1, 1)
     assert pr.plan("gru", pr.make_shape(1, 1, 64)) == (1, 1, 1)
-    assert pr.plan("lstm", pr.make_shape(8, 4096, 1024)) == (8, 8, 1)
+    assert pr.plan("lstm", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
+    assert pr.plan("lstm", pr.make_shape(16, 2048, 4096)) == (16, 2, 1)
     assert pr.plan("lstm", pr.make_shape(16, 2048, 4096), adjoint=True) == (8, 4, 1)
     # forced tiling, ragged T
     n = pr.make_newton(steps_per_lane=1, waves_per_block=1)
     assert pr.plan("gru", pr.make_shape(2, 3 * 64 + 7, 3), n) == (1, 1, 4)
 
 
-@pytest.mark.parametrize("K,W", [(3, 1), (32, 1), (1, 16), (1, 3), (-1, 1)])
+@pytest.mark.parametrize("K,W", [(3, 1), (64, 1), (1, 16), (1, 3), (-1, 1), (32, 4)])
 def test_plan_rejects_unsupported_tiling(K, W):
     n = pr.make_newton(steps_per_lane=K, waves_per_block=W)
     with pytest.raises(pr.PararnnError) as e:
         pr.plan("gru", pr.make_shape(1, 100, 1), n)
     assert e.value.status == 2
+
+
+def test_wide_lane_tiling_is_gru_forward_only():
+    n = pr.make_newton(steps_per_lane=32, waves_per_block=2)
+    assert pr.plan("gru", pr.make_shape(1, 4096, 1), n) == (32, 2, 1)
+    for cell, adj in [("lstm", False), ("gru", True), ("lstm", True)]:
+        with pytest.raises(pr.PararnnError) as e:
+            pr.plan(cell, pr.make_shape(1, 4096, 1), n, adjoint=adj)
+        assert e.value.status == 2
 
 
 def test_workspace_sizes():
