@@ -78,8 +78,10 @@ typedef struct {
      * residual is always evaluated. */
     float tol;
     int32_t max_iters;        /* >= 0                                          */
-    int32_t steps_per_lane;   /* K: 0 = automatic, else 1, 2, 4, 8 or 16       */
-    int32_t waves_per_block;  /* W: 0 = automatic, else 1, 2, 4, 8 or 16       */
+    int32_t steps_per_lane;   /* K: 0 = automatic, else 1, 2, 4, 8, 16, or 32
+                                 (ParaGRU forward solve with W = 1 or 2 only)  */
+    int32_t waves_per_block;  /* W: 0 = automatic, else 1, 2, 4 or 8; one
+                                 workgroup covers 64 * K * W time steps       */
     int32_t init_from_output; /* 1: Newton starts from the values already in
                                  the output planes; 0: from s = 0             */
 } pararnn_newton_t;
@@ -156,6 +158,33 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
                                  float *const *du, float *da, float *const *ds0,
                                  float *const *lam, const pararnn_newton_t *opt,
                                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The linear recurrence of a Newton iteration on its own, for callers that
+ * assemble (A_t, b_t) themselves: "Параллельность RNN?" (forpes.ru), §1.3,
+ * level 1 (forward substitution) solved as in level 2 (associative scan of
+ * affine maps); the "parallel reduction" tier of the voguetech.ru ParaRNN
+ * article ("Три уровня производительности", item 2).  Per channel (b, d):
+ *   reverse = 0:  x_t = A_t x_{t-1} + b_t,  t = 1..T,  x_0 given
+ *   reverse = 1:  x_t = A_t x_{t+1} + b_t,  t = T..1,  x_{T+1} given
+ *   state_size : 1 (A_t scalar) or 2 (A_t a 2x2 block)
+ *   A          : state_size^2 planes [B][D][T] float32 (u_stride_*), 2x2 blocks
+ *                row-major (a00, a01, a10, a11)
+ *   b          : state_size planes [B][D][T] float32 (u_stride_*)
+ *   x0         : NULL (boundary value zero) or state_size pointers to [B][D]
+ *   x          : state_size planes [B][D][T] float32 out (s_stride_*)
+ *   opt        : only steps_per_lane / waves_per_block are read (may be NULL)
+ *   ws         : pararnn_scan_workspace_bytes(...) bytes (0 is possible)
+ * Same conventions as above: device pointers, caller's stream, no
+ * allocation, argument checks before any HIP call.
+ */
+size_t pararnn_scan_workspace_bytes(int32_t state_size, const pararnn_shape_t *shape,
+                                    const pararnn_newton_t *opt);
+pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
+                              const float *const *A, const float *const *b,
+                              const float *const *x0, float *const *x, int32_t reverse,
+                              const pararnn_newton_t *opt, void *ws, size_t ws_bytes,
+                              void *stream);
 
 /* Static description of a status code. */
 const char *pararnn_status_string(pararnn_status_t status);

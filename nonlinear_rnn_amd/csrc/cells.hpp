@@ -58,9 +58,9 @@ struct GruCell {
         const float c = tanh_q(fmaf_(p.qc, rh, u[2]));
         const float cmh = c - hp;
         const float b = fmaf_(z, cmh, hp - h_.x);   // f - h_t = -r_t, f = (1 - z) h + z c
-        // df/dh = (1 - z) + z [ (c - h)(1 - z) a_z + (1 - c^2) a_c r (1 + h (1 - r) a_r) ]
+        // df/dh = (1 - z) + z [ (c - h)(1 - z) a_z + (1 - c^2) a_c (r + h a_r r(1 - r)) ]
         const float omz = 1.0f - z;
-        const float dcr = fmaf_(-c, c, 1.0f) * p.ac * (r * fmaf_(hp * (1.0f - r), p.ar, 1.0f));
+        const float dcr = (fmaf_(-c, c, 1.0f) * p.ac) * fmaf_(hp * p.ar, fmaf_(-r, r, r), r);
         const float J = fmaf_(z, fmaf_(cmh * omz, p.az, dcr), omz);
         return {J, b};
     }
@@ -109,13 +109,14 @@ struct LstmCell {
         // dc'/dh = c f(1-f) a_f + g i(1-i) a_i + i (1-g^2) a_g
         // dh'/dc = o (1 - tanh^2 c') f
         // dh'/dh = tanh(c') o(1-o) a_o + o (1 - tanh^2 c') dc'/dh
-        const float dcdh = fmaf_(cp * (f * (1.0f - f)), p.af,
-                                 fmaf_(g * (i * (1.0f - i)), p.ai, (i * fmaf_(-g, g, 1.0f)) * p.ag));
+        // x(1 - x) as one FMA: fma(-x, x, x)
+        const float dcdh = fmaf_(cp * fmaf_(-f, f, f), p.af,
+                                 fmaf_(g * fmaf_(-i, i, i), p.ai, (i * fmaf_(-g, g, 1.0f)) * p.ag));
         const float ot = o * fmaf_(-tc, tc, 1.0f);
         m.a00 = f;
         m.a01 = dcdh;
         m.a10 = ot * f;
-        m.a11 = fmaf_(tc * (o * (1.0f - o)), p.ao, ot * dcdh);
+        m.a11 = fmaf_(tc * fmaf_(-o, o, o), p.ao, ot * dcdh);
         return m;
     }
 };

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "adjoint.hpp"
+#include "scan_kernel.hpp"
 #include "solve.hpp"
 
 namespace pararnn {
@@ -34,6 +35,10 @@ PARARNN_DECLARE_LAUNCHERS(lstm_f32)
 PARARNN_DECLARE_LAUNCHERS(lstm_bf16)
 #undef PARARNN_DECLARE_LAUNCHERS
 
+// Standalone scan: state size 1 or 2, forward or reverse.
+hipError_t launch_scan(int S, int K, int W, bool reverse, int64_t groups, hipStream_t st,
+                       const ScanArgs &a);
+
 #define PARARNN_BASE_KW(X)                                                                      \
     X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 1) X(4, 2) X(4, 4)    \
         X(4, 8) X(8, 1) X(8, 2) X(8, 4) X(8, 8) X(16, 1) X(16, 2) X(16, 4) X(16, 8)
@@ -52,7 +57,7 @@ PARARNN_DECLARE_LAUNCHERS(lstm_bf16)
         break;
 
 // EXTRA(X) lists tilings beyond the base set for this cell.
-#define PARARNN_DEFINE_LAUNCHERS(NAME, CELL, BF16, EXTRA)                                       \
+#define PARARNN_DEFINE_LAUNCHERS(NAME, CELL, BF16, EXTRA)                                  \
     hipError_t launch_newton_##NAME(int K, int W, bool full, int64_t groups, hipStream_t st,    \
                                     const SolveArgs &a)                                         \
     {                                                                                           \

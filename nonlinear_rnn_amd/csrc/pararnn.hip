@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #define PARARNN_DEFINE_AUX_KERNELS
@@ -64,9 +65,12 @@ bool opt_k_w_unset(const pararnn_newton_t *opt)
 // Default tiling: the smallest block capacity P = 64 W K that covers T, from
 // a list ordered by preference; past the largest one, several time blocks
 // per channel.
+// kind: 0 = Newton solve, 1 = adjoint, 2 = standalone scan (cell selects the
+// state size: GRU 1, LSTM 2).
 pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
-                           const pararnn_newton_t *opt, int adjoint, Plan &pl)
+                           const pararnn_newton_t *opt, int kind, Plan &pl)
 {
+    const bool adjoint = kind != 0;
     pararnn_status_t st = check_shape(sh);
     if (st != PARARNN_OK) return st;
     int K = opt ? opt->steps_per_lane : 0;
@@ -77,8 +81,14 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
         static const int gru_kw[][2] = {{16, 4}, {16, 2}, {16, 1}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
         static const int lstm_kw[][2] = {{16, 4}, {16, 2}, {16, 1}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
         static const int adj_kw[][2] = {{8, 4}, {8, 2}, {8, 1}, {4, 1}, {2, 1}, {1, 1}};
-        const int(*tab)[2] = adjoint ? adj_kw : (cell == PARARNN_LSTM ? lstm_kw : gru_kw);
-        const int n = adjoint ? 6 : 7;
+        // One pass and no Newton state: the scan keeps a channel in one
+        // workgroup as long as it can (up to 8192 steps), since a time-block
+        // hand-off costs more than the rest of the pass.
+        static const int scan_kw[][2] = {{16, 8}, {8, 8}, {8, 4}, {8, 2},
+                                         {8, 1},  {4, 1}, {2, 1}, {1, 1}};
+        const int(*tab)[2] =
+            kind == 2 ? scan_kw : adjoint ? adj_kw : (cell == PARARNN_LSTM ? lstm_kw : gru_kw);
+        const int n = kind == 2 ? 8 : adjoint ? 6 : 7;
         int pick = 0;
         for (int i = 0; i < n; ++i) {
             const int kk = K ? K : tab[i][0], ww = W ? W : tab[i][1];
@@ -251,9 +261,105 @@ AdjWs adj_ws_layout(pararnn_cell_t cell, const Plan &pl)
     return w;
 }
 
+struct ScanWs {
+    size_t ticket = 0, flags = 0, records = 0, total = 0;
+};
+
+ScanWs scan_ws_layout(int S, const Plan &pl)
+{
+    ScanWs w;
+    if (pl.nb <= 1) return w;
+    size_t off = 0;
+    w.ticket = off;
+    off += kAlign;
+    w.flags = off;
+    off = align_up(off + (size_t)pl.units * sizeof(int32_t));
+    w.records = off;
+    const int rf = S == 2 ? MapRec<Map2>::kFloats : MapRec<Map1>::kFloats;
+    off = align_up(off + (size_t)pl.units * rf * sizeof(float));
+    w.total = off;
+    return w;
+}
+
+// The scan is built for the adjoint's tilings (one pass, no Newton state).
+pararnn_status_t make_scan_plan(int32_t S, const pararnn_shape_t *sh, const pararnn_newton_t *opt,
+                                Plan &pl)
+{
+    if (S != 1 && S != 2) return PARARNN_ERR_INVALID;
+    return make_plan(S == 2 ? PARARNN_LSTM : PARARNN_GRU, sh, opt, 2, pl);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t pararnn_scan_workspace_bytes(int32_t state_size, const pararnn_shape_t *shape,
+                                    const pararnn_newton_t *opt)
+{
+    Plan pl;
+    if (make_scan_plan(state_size, shape, opt, pl) != PARARNN_OK) return 0;
+    return scan_ws_layout(state_size, pl).total;
+}
+
+pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
+                              const float *const *Am, const float *const *bv,
+                              const float *const *x0, float *const *x, int32_t reverse,
+                              const pararnn_newton_t *opt, void *ws, size_t ws_bytes, void *stream)
+{
+    Plan pl;
+    pararnn_status_t st = make_scan_plan(state_size, shape, opt, pl);
+    if (st != PARARNN_OK) return st;
+    if (reverse != 0 && reverse != 1) return PARARNN_ERR_INVALID;
+    const int S = state_size;
+    const bool work = pl.channels > 0 && shape->T > 0;
+    if (!work) return PARARNN_OK;
+    if (!Am || !bv || !x) return PARARNN_ERR_INVALID;
+    for (int i = 0; i < S * S; ++i)
+        if (!Am[i]) return PARARNN_ERR_INVALID;
+    for (int c = 0; c < S; ++c)
+        if (!bv[c] || !x[c] || (x0 && !x0[c])) return PARARNN_ERR_INVALID;
+    const ScanWs wl = scan_ws_layout(S, pl);
+    if (wl.total > 0 && (!ws || ws_bytes < wl.total || !aligned16(ws))) return PARARNN_ERR_WORKSPACE;
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+
+    ScanArgs A;
+    std::memset(&A, 0, sizeof(A));
+    for (int i = 0; i < S * S; ++i) A.A[i] = Am[i];
+    for (int c = 0; c < S; ++c) {
+        A.b[c] = bv[c];
+        A.x[c] = x[c];
+        A.x0[c] = x0 ? x0[c] : nullptr;
+    }
+    A.B = shape->B;
+    A.T = shape->T;
+    A.D = shape->D;
+    A.isb = shape->u_stride_b;
+    A.isd = shape->u_stride_d;
+    A.osb = shape->s_stride_b;
+    A.osd = shape->s_stride_d;
+    A.channels = pl.channels;
+    A.nb = (int32_t)pl.nb;
+    bool iv = (shape->T % 4 == 0) && (shape->u_stride_b % 4 == 0) && (shape->u_stride_d % 4 == 0);
+    for (int i = 0; i < S * S; ++i) iv = iv && aligned16(Am[i]);
+    for (int c = 0; c < S; ++c) iv = iv && aligned16(bv[c]);
+    bool ov = (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) && (shape->s_stride_d % 4 == 0);
+    for (int c = 0; c < S; ++c) ov = ov && aligned16(x[c]);
+    A.in_vec = iv ? 1 : 0;
+    A.out_vec = ov ? 1 : 0;
+    if (wl.total > 0) {
+        char *base = static_cast<char *>(ws);
+        A.ticket = reinterpret_cast<uint32_t *>(base + wl.ticket);
+        A.flags = reinterpret_cast<int32_t *>(base + wl.flags);
+        A.records = reinterpret_cast<float *>(base + wl.records);
+        const int tpb = 256;
+        hipLaunchKernelGGL(scan_init_kernel, dim3((unsigned)((pl.units + tpb - 1) / tpb)), dim3(tpb),
+                           0, strm, A, pl.units);
+        if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+    return launch_scan(S, pl.K, pl.W, reverse != 0, groups, strm, A) == hipSuccess ? PARARNN_OK
+                                                                                  : PARARNN_ERR_HIP;
+}
 
 const char *pararnn_status_string(pararnn_status_t s)
 {
@@ -273,7 +379,7 @@ pararnn_status_t pararnn_plan(pararnn_cell_t cell, const pararnn_shape_t *shape,
 {
     if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return PARARNN_ERR_INVALID;
     Plan pl;
-    pararnn_status_t st = make_plan(cell, shape, opt, adjoint, pl);
+    pararnn_status_t st = make_plan(cell, shape, opt, adjoint ? 1 : 0, pl);
     if (st != PARARNN_OK) return st;
     if (K) *K = pl.K;
     if (W) *W = pl.W;
@@ -286,7 +392,7 @@ size_t pararnn_workspace_bytes(pararnn_cell_t cell, const pararnn_shape_t *shape
 {
     if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return 0;
     Plan pl;
-    if (make_plan(cell, shape, opt, adjoint, pl) != PARARNN_OK) return 0;
+    if (make_plan(cell, shape, opt, adjoint ? 1 : 0, pl) != PARARNN_OK) return 0;
     if (adjoint) return adj_ws_layout(cell, pl).total;
     if (opt && (opt->max_iters < 0 || opt->max_iters > kMaxIters)) return 0;
     return solve_ws_layout(cell, pl, opt).total;

@@ -36,6 +36,12 @@ __device__ __forceinline__ float tanh_q(float q) { return fmaf_(2.0f, rcpf_(1.0f
 // float order and every NaN pattern is larger than +inf, so an unsigned max
 // over these never loses a NaN (IEEE fmax would).
 __device__ __forceinline__ uint32_t absbits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+// Running max of |x| that propagates NaN (IEEE 754-2019 maximum; CDNA4 has
+// it as v_maximum3_f32 with |.| source modifiers, two new values per op).
+__device__ __forceinline__ float max_abs(float m, float x)
+{
+    return __builtin_elementwise_maximum(m, __builtin_fabsf(x));
+}
 
 // ---------------------------------------------------------- affine maps ---
 // A map x -> A x + b.  compose(L, E) applies E first, then L:
@@ -55,8 +61,8 @@ __device__ __forceinline__ Map1 compose(const Map1 &L, const Map1 &E)
 struct Vec1 {
     float x;
 };
-// max |b| of a map's residual part, as unsigned bits (see absbits)
-__device__ __forceinline__ uint32_t resbits(const Map1 &m) { return absbits(m.b); }
+// running max of |b| (the residual part of a step map), NaN-propagating
+__device__ __forceinline__ float resmax(float mx, const Map1 &m) { return max_abs(mx, m.b); }
 // the identity where `keep` is false (select, no branch)
 __device__ __forceinline__ Map1 keep_or_identity(const Map1 &m, bool keep)
 {
@@ -82,7 +88,10 @@ __device__ __forceinline__ Map2 compose(const Map2 &L, const Map2 &E)
 struct Vec2 {
     float x0, x1;
 };
-__device__ __forceinline__ uint32_t resbits(const Map2 &m) { return max(absbits(m.b0), absbits(m.b1)); }
+__device__ __forceinline__ float resmax(float mx, const Map2 &m)
+{
+    return max_abs(max_abs(mx, m.b0), m.b1);
+}
 __device__ __forceinline__ Map2 keep_or_identity(const Map2 &m, bool keep)
 {
     return {keep ? m.a00 : 1.0f, keep ? m.a01 : 0.0f, keep ? m.a10 : 0.0f,
@@ -190,11 +199,21 @@ __device__ __forceinline__ int32_t load_flag(const int32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// s_waitcnt through the builtin rather than inline asm, so the compiler's own
+// wait insertion sees it and does not add a second, blanket vmcnt(0) later
+// (it cannot look inside an asm block).  gfx9 immediate: vmcnt in bits
+// [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]; all-ones = no wait.  The
+// empty asm keeps the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void wait_vm()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    asm volatile("" ::: "memory");
+}
 // Flag store ordered after every earlier store of this lane: wait until those
 // have completed (reached the coherence point), then write the flag.
 __device__ __forceinline__ void publish_flag(int32_t *p, int32_t v)
 {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm();
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // After a flag read has returned the awaited value: keep the compiler from

@@ -41,6 +41,10 @@ namespace pararnn {
 
 constexpr int32_t kStopBase = 1 << 24;
 
+#ifndef PARARNN_GRU_MAPS_IN_LDS
+#define PARARNN_GRU_MAPS_IN_LDS 1
+#endif
+
 struct SolveArgs {
     const void *u[4];
     const float *a;
@@ -282,19 +286,175 @@ struct Slot {
     uint32_t mx;
 };
 
-// FULL: every time block lies wholly inside [0, T) (T a multiple of the
-// block capacity), so the hot loop carries no per-step masks at all; the
-// other variant turns steps past T into identity maps by selection.
-template <class Cell, int K, int W, bool BF16, bool FULL>
-__global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
+// Where the lane's running compositions wait between up-sweep and down-sweep:
+// in VGPRs, or (ParaGRU: 2 floats per step) in LDS, which frees 2K VGPRs and
+// lets 4 workgroups share a CU.
+template <class Cell, int K, bool FULL>
+struct MapStore {
+    static constexpr bool kLds =
+        PARARNN_GRU_MAPS_IN_LDS && sizeof(typename Cell::Map) == 8 && K >= 8;
+    // the unmasked ParaGRU loop then fits 4 waves per SIMD without spills
+    static constexpr int kMinWavesPerEu = (kLds && FULL && K <= 16) ? 4 : 1;
+};
+
+// LDS of the Newton loop: wave aggregates (double-buffered by iteration
+// parity) and, optionally, the running compositions.
+template <class Cell, int K, int W, bool MAPS_LDS>
+struct LoopSmem {
+    Slot<typename Cell::Map> slots[2][W];
+    typename Cell::Map mlds[MAPS_LDS ? K : 1][MAPS_LDS ? W * kWave : 1];
+};
+
+// Lane's K steps of every gate, pre-scaled for the exp2-based gates.
+template <class Cell, int K, bool BF16>
+__device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uoff, int64_t t0,
+                                                 float (&u)[K][Cell::G])
+{
+#pragma unroll
+    for (int g = 0; g < Cell::G; ++g) {
+        float tmp[K];
+        load_steps<K, BF16>(A.u[g], uoff, t0, A.T, A.u_vec != 0, tmp);
+        const float sc = Cell::uscale(g);
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) u[kk][g] = tmp[kk] * sc;
+    }
+}
+
+// The whole Newton solve of one work unit — channel `ch`, time block `k` —
+// from the lane's pre-scaled projections `u`, its copy `hin` of the state
+// before its first step and the Newton start `s`; writes the converged states
+// and folds the unit into the info record.
+template <class Cell, int K, int W, bool FULL, bool MAPS_LDS>
+__device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32_t k,
+                                           const typename Cell::Coef &cf,
+                                           const float (&u)[K][Cell::G],
+                                           typename Cell::Vec (&s)[K], typename Cell::Vec hin,
+                                           LoopSmem<Cell, K, W, MAPS_LDS> &sm)
 {
     using M = typename Cell::Map;
     using V = typename Cell::Vec;
-    constexpr int G = Cell::G, S = Cell::S;
+    constexpr int S = Cell::S;
     constexpr int P = W * kWave * K;
     constexpr int RF = MapRec<M>::kFloats;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t unit = ch * A.nb + k;
+    const int64_t b = ch / A.D, d = ch - b * A.D;
+    const int64_t T = A.T;
+    const int64_t tb0 = (int64_t)k * P;
+    const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
+    const bool multi = A.nb > 1;
+    const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
+    const bool full = FULL || tb0 + P <= T;  // uniform over the workgroup
 
-    __shared__ Slot<M> slots[2][W];
+    const uint32_t tolb = __float_as_uint(A.tol);
+    M m[MAPS_LDS ? 1 : K];  // running composition of the lane's steps 0..kk
+    int32_t it = 0;
+    uint32_t bmx = 0;
+    for (;; ++it) {
+        // ---- residual, Jacobian and lane up-sweep.  Blocks that lie wholly
+        // inside [0, T) take a path without per-step masks; the ragged last
+        // block turns steps past T into identity maps by selection.
+        float mxf = 0.0f;
+        M agg = identity_map(M{});
+        V prev = hin;
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) {
+            M mk = Cell::step_map(cf, u[kk], prev, s[kk]);
+            if (!full) mk = keep_or_identity(mk, t0 + kk < T);
+            mxf = resmax(mxf, mk);
+            prev = s[kk];
+            agg = kk == 0 ? mk : compose(mk, agg);
+            if constexpr (MAPS_LDS)
+                sm.mlds[kk][threadIdx.x] = agg;
+            else
+                m[kk] = agg;
+        }
+        // ---- wave scan, then block exchange through LDS
+        const M inc = wave_scan_inclusive(agg);
+        const M exc = wave_shift_up(inc);
+        // |r| bit patterns: unsigned order = float order, NaN above +inf
+        const uint32_t wmx = wave_max_to_last(__float_as_uint(mxf));
+        const int par = it & 1;
+        if (lane == kWave - 1) {
+            sm.slots[par][wave].agg = inc;
+            sm.slots[par][wave].mx = wmx;
+        }
+        __syncthreads();
+        bmx = sm.slots[par][0].mx;
+        M blk = sm.slots[par][0].agg;
+#pragma unroll
+        for (int j = 1; j < W; ++j) {
+            bmx = max(bmx, sm.slots[par][j].mx);
+            blk = compose(sm.slots[par][j].agg, blk);
+        }
+        const uint32_t cbit = bmx < tolb ? 1u : 0u;
+        const bool at_cap = (it == A.cap);
+        if (multi && threadIdx.x == 0) {
+            rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
+            publish_flag(A.flags + unit, it + 1);
+        }
+        if (at_cap) break;
+        V din = vzero<V>();
+        bool pred_stopped = true;
+        if (multi && k > 0) look_back<M, V>(A, ch, k, it, din, pred_stopped);
+        if (cbit && pred_stopped) {
+            if (multi && threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
+            break;
+        }
+        // ---- down-sweep from the carries, Newton update
+        V dw = din;
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j)
+            if (j < wave) dw = apply(sm.slots[par][j].agg, dw);
+        const V dl = apply(exc, dw);
+        const V dout = (multi && last_lane_of_block) ? apply(blk, din) : apply(inc, dw);
+        hin = vadd(hin, dl);
+        // m[kk] holds the lane's running composition of steps 0..kk, so every
+        // step's correction comes straight from the lane carry-in (no serial
+        // chain); the last step takes the carry the next lane also sees.
+#pragma unroll
+        for (int kk = 0; kk < K - 1; ++kk) {
+            if constexpr (MAPS_LDS)
+                s[kk] = vadd(s[kk], apply(sm.mlds[kk][threadIdx.x], dl));
+            else
+                s[kk] = vadd(s[kk], apply(m[kk], dl));
+        }
+        s[K - 1] = vadd(s[K - 1], dout);
+    }
+
+    // ---- converged states out
+    const int64_t soff = b * A.ssb + d * A.ssd;
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        float tmp[K];
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) tmp[kk] = vget(s[kk], c);
+        store_steps<K>(A.s[c] + soff, t0, T, A.s_vec != 0, tmp);
+    }
+    if (A.info && threadIdx.x == 0) {
+        pararnn_info_t *inf = A.info;
+        atomicMax(&inf->iters, it);
+        if (!(bmx < tolb)) atomicAnd(&inf->converged, 0);
+        atomicMax(reinterpret_cast<unsigned int *>(&inf->max_abs_res), bmx);
+        if (bmx > 0x7f800000u) atomicOr(&inf->nan_seen, 1);
+        atomicAdd(reinterpret_cast<unsigned long long *>(&inf->iters_sum),
+                  (unsigned long long)it);
+    }
+}
+
+// One work unit per workgroup.  Serves every case: several time blocks per
+// channel (dynamic tickets), ragged T, warm starts.
+template <class Cell, int K, int W, bool BF16, bool FULL>
+__global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, FULL>::kMinWavesPerEu))
+    newton_kernel(SolveArgs A)
+{
+    using V = typename Cell::Vec;
+    constexpr int G = Cell::G, S = Cell::S;
+    constexpr int P = W * kWave * K;
+    constexpr bool kMapsLds = MapStore<Cell, K, FULL>::kLds;
+
+    __shared__ LoopSmem<Cell, K, W, kMapsLds> sm;
     __shared__ int64_t s_ticket;
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -316,29 +476,15 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
     const int64_t T = A.T;
     const int64_t tb0 = (int64_t)k * P;
     const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
-    const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
-    const bool full = FULL || tb0 + P <= T;  // uniform over the workgroup
 
     const typename Cell::Coef cf = Cell::coef(A.a, A.D, d);
-
-    // Projections, pre-scaled for the exp2-based gates.
     float u[K][G];
-    {
-        const int64_t uoff = b * A.usb + d * A.usd;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float tmp[K];
-            load_steps<K, BF16>(A.u[g], uoff, t0, T, A.u_vec != 0, tmp);
-            const float sc = Cell::uscale(g);
-#pragma unroll
-            for (int kk = 0; kk < K; ++kk) u[kk][g] = tmp[kk] * sc;
-        }
-    }
+    load_projections<Cell, K, BF16>(A, b * A.usb + d * A.usd, t0, u);
 
     // Newton start and the lane's copy of the state just before it.
     const int64_t soff = b * A.ssb + d * A.ssd;
     V s[K];
-    V hin;
+    V hin = vzero<V>();
     if (A.init_from_output) {
 #pragma unroll
         for (int c = 0; c < S; ++c) {
@@ -347,7 +493,6 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) vset(s[kk], c, tmp[kk]);
         }
-        hin = vzero<V>();
 #pragma unroll
         for (int c = 0; c < S; ++c) {
             float x = 0.0f;
@@ -362,107 +507,12 @@ __global__ void __launch_bounds__(W * kWave) newton_kernel(SolveArgs A)
     } else {
 #pragma unroll
         for (int kk = 0; kk < K; ++kk) s[kk] = vzero<V>();
-        hin = vzero<V>();
         if (t0 == 0) {
 #pragma unroll
             for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
         }
     }
-
-    const uint32_t tolb = __float_as_uint(A.tol);
-    M m[K];  // running composition of the lane's steps 0..kk
-    int32_t it = 0;
-    uint32_t bmx = 0;
-    for (;; ++it) {
-        // ---- residual, Jacobian and lane up-sweep.  Blocks that lie wholly
-        // inside [0, T) take a path without per-step masks; the ragged last
-        // block turns steps past T into identity maps by selection.
-        uint32_t mx = 0;
-        M agg = identity_map(M{});
-        V prev = hin;
-        if (full) {
-#pragma unroll
-            for (int kk = 0; kk < K; ++kk) {
-                const M mk = Cell::step_map(cf, u[kk], prev, s[kk]);
-                mx = max(mx, resbits(mk));
-                prev = s[kk];
-                agg = kk == 0 ? mk : compose(mk, agg);
-                m[kk] = agg;
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < K; ++kk) {
-                const M mk = keep_or_identity(Cell::step_map(cf, u[kk], prev, s[kk]), t0 + kk < T);
-                mx = max(mx, resbits(mk));
-                prev = s[kk];
-                agg = kk == 0 ? mk : compose(mk, agg);
-                m[kk] = agg;
-            }
-        }
-        // ---- wave scan, then block exchange through LDS
-        const M inc = wave_scan_inclusive(agg);
-        const M exc = wave_shift_up(inc);
-        const uint32_t wmx = wave_max_to_last(mx);
-        const int par = it & 1;
-        if (lane == kWave - 1) {
-            slots[par][wave].agg = inc;
-            slots[par][wave].mx = wmx;
-        }
-        __syncthreads();
-        bmx = slots[par][0].mx;
-        M blk = slots[par][0].agg;
-#pragma unroll
-        for (int j = 1; j < W; ++j) {
-            bmx = max(bmx, slots[par][j].mx);
-            blk = compose(slots[par][j].agg, blk);
-        }
-        const uint32_t cbit = bmx < tolb ? 1u : 0u;
-        const bool at_cap = (it == A.cap);
-        if (A.nb > 1 && threadIdx.x == 0) {
-            rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
-            publish_flag(A.flags + unit, it + 1);
-        }
-        if (at_cap) break;
-        V din = vzero<V>();
-        bool pred_stopped = true;
-        if (k > 0) look_back<M, V>(A, ch, k, it, din, pred_stopped);
-        if (cbit && pred_stopped) {
-            if (A.nb > 1 && threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
-            break;
-        }
-        // ---- down-sweep from the carries, Newton update
-        V dw = din;
-#pragma unroll
-        for (int j = 0; j < W - 1; ++j)
-            if (j < wave) dw = apply(slots[par][j].agg, dw);
-        const V dl = apply(exc, dw);
-        const V dout = (A.nb > 1 && last_lane_of_block) ? apply(blk, din) : apply(inc, dw);
-        hin = vadd(hin, dl);
-        // m[kk] holds the lane's running composition of steps 0..kk, so every
-        // step's correction comes straight from the lane carry-in (no serial
-        // chain); the last step takes the carry the next lane also sees.
-#pragma unroll
-        for (int kk = 0; kk < K - 1; ++kk) s[kk] = vadd(s[kk], apply(m[kk], dl));
-        s[K - 1] = vadd(s[K - 1], dout);
-    }
-
-    // ---- converged states out
-#pragma unroll
-    for (int c = 0; c < S; ++c) {
-        float tmp[K];
-#pragma unroll
-        for (int kk = 0; kk < K; ++kk) tmp[kk] = vget(s[kk], c);
-        store_steps<K>(A.s[c] + soff, t0, T, A.s_vec != 0, tmp);
-    }
-    if (A.info && threadIdx.x == 0) {
-        pararnn_info_t *inf = A.info;
-        atomicMax(&inf->iters, it);
-        if (!(bmx < tolb)) atomicAnd(&inf->converged, 0);
-        atomicMax(reinterpret_cast<unsigned int *>(&inf->max_abs_res), bmx);
-        if (bmx > 0x7f800000u) atomicOr(&inf->nan_seen, 1);
-        atomicAdd(reinterpret_cast<unsigned long long *>(&inf->iters_sum),
-                  (unsigned long long)it);
-    }
+    solve_unit<Cell, K, W, FULL, kMapsLds>(A, ch, k, cf, u, s, hin, sm);
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit

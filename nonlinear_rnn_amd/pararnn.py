@@ -6,7 +6,7 @@ and the current HIP stream into the pointers and sizes the ABI takes, and
 raises on a non-OK status.  There is no fallback: if the library or a GPU
 is missing, the calls raise.
 
-Names follow the ABI: ``solve_gru``, ``solve_lstm``, ``adjoint``,
+Names follow the ABI: ``solve_gru``, ``solve_lstm``, ``adjoint``, ``scan``,
 ``workspace_bytes``, ``plan``.
 """
 import ctypes
@@ -71,6 +71,10 @@ def load():
     lib.pararnn_solve_lstm.restype = i32
     lib.pararnn_solve_lstm.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, P(Newton), vp,
                                        vp, sz, vp]
+    lib.pararnn_scan_workspace_bytes.restype = sz
+    lib.pararnn_scan_workspace_bytes.argtypes = [i32, P(Shape), P(Newton)]
+    lib.pararnn_scan.restype = i32
+    lib.pararnn_scan.argtypes = [i32, P(Shape), vp, vp, vp, vp, i32, P(Newton), vp, sz, vp]
     lib.pararnn_adjoint.restype = i32
     lib.pararnn_adjoint.argtypes = [i32, P(Shape), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                     P(Newton), vp, sz, vp]
@@ -273,3 +277,31 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
                                ctypes.byref(newton), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream_handle(stream)))
     return dict(du=du, da=da, ds0=ds0, lam=lam)
+
+
+def scan(A, b, x0=None, *, reverse=False, out=None, steps_per_lane=0, waves_per_block=0,
+         workspace=None, stream=None):
+    """Linear recurrence x_t = A_t x_{t-1} + b_t (or, reversed, x_t = A_t
+    x_{t+1} + b_t) per channel.  A: S*S float32 planes [B][D][T] (2x2 blocks
+    row-major), b: S planes, x0: None or S [B][D] boundary values.  Returns
+    the S planes of x."""
+    lib = load()
+    A, b = list(A), list(b)
+    S = len(b)
+    if S not in (1, 2) or len(A) != S * S:
+        raise ValueError("state size must be 1 or 2 (A has S*S planes, b has S)")
+    B, D, T = b[0].shape
+    dev = b[0].device
+    ins = _strides(A + b, "A/b") or (D * T, T)
+    if out is None:
+        out = [torch.empty((B, D, T), dtype=torch.float32, device=dev) for _ in range(S)]
+    outs = _strides(out, "x") or (D * T, T)
+    shape = make_shape(B, T, D, ins, outs)
+    newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
+    nws = int(lib.pararnn_scan_workspace_bytes(S, ctypes.byref(shape), ctypes.byref(newton)))
+    ws = workspace if workspace is not None else _ws.get(nws, dev)
+    _check(lib.pararnn_scan(S, ctypes.byref(shape), _ptr_array(A), _ptr_array(b),
+                            _ptr_array(x0) if x0 is not None else None, _ptr_array(out),
+                            1 if reverse else 0, ctypes.byref(newton), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream_handle(stream)))
+    return out

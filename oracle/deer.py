@@ -198,6 +198,21 @@ def solve_closed_form(A, b):
     return x
 
 
+def linear_recurrence(A, b, x0=None, reverse=False):
+    """The linear recurrence on its own ("Параллельность RNN?", §1.3,
+    level 1), step by step: x_t = A_t x_{t-1} + b_t for t = 1..T from x_0, or
+    with ``reverse`` x_t = A_t x_{t+1} + b_t for t = T..1 from x_{T+1}
+    (``x0`` [n, S] is that boundary value; None means zero)."""
+    n, T, S = b.shape
+    x = np.empty_like(b)
+    prev = np.zeros((n, S)) if x0 is None else np.array(x0, np.float64)
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    for t in order:
+        prev = np.einsum("nij,nj->ni", A[:, t], prev) + b[:, t]
+        x[:, t] = prev
+    return x
+
+
 SOLVERS = {
     "serial": solve_forward_substitution,
     "tree": solve_tree_scan,

@@ -86,6 +86,21 @@ def test_workspace_sizes():
     assert pr.workspace_bytes(7, pr.make_shape(1, 1, 1), n) == 0
 
 
+def test_scan_keeps_channels_in_one_workgroup_up_to_8192_steps():
+    """The standalone scan's default tiling: no time blocks (workspace 0) up
+    to 8192 steps, then 8192-step blocks with records and flags."""
+    lib = pr.load()
+    n = pr.make_newton(0.0, 0)
+    for S in (1, 2):
+        for T in (1, 4096, 8192):
+            sh = pr.make_shape(2, T, 3)
+            assert lib.pararnn_scan_workspace_bytes(S, ctypes.byref(sh), ctypes.byref(n)) == 0
+        sh = pr.make_shape(2, 8193, 3)
+        assert lib.pararnn_scan_workspace_bytes(S, ctypes.byref(sh), ctypes.byref(n)) > 0
+    assert lib.pararnn_scan_workspace_bytes(3, ctypes.byref(pr.make_shape(2, 9000, 3)),
+                                            ctypes.byref(n)) == 0
+
+
 def _call_gru(shape, newton, u=(1, 1, 1), a=1, h0=1, h=1, ws=None, nws=0):
     lib = pr.load()
     arr = (ctypes.c_void_p * 3)(*[x or None for x in u])

@@ -406,3 +406,33 @@ def test_bptt_matches_finite_differences(cell):
                                        rtol=2e-5, atol=2e-6)
     for k, plane in enumerate(inp.s0):
         np.testing.assert_allclose(fd(plane, (0, 1)), ds0[k][0, 1], rtol=2e-5, atol=2e-6)
+
+
+@pytest.mark.parametrize("S", [1, 2])
+@pytest.mark.parametrize("reverse", [False, True])
+@pytest.mark.parametrize("T", [1, 2, 7, 33])
+def test_linear_recurrence_is_dense_solve(S, reverse, T):
+    """x_t - A_t x_{t-1} = b_t (x_0 given) as one block-bidiagonal system,
+    solved densely; the reverse recurrence is the same system with time
+    flipped."""
+    rng = np.random.default_rng(131 + T)
+    n = 3
+    A = rng.uniform(-1.1, 1.1, (n, T, S, S))
+    b = rng.standard_normal((n, T, S))
+    x0 = rng.standard_normal((n, S))
+    x = deer.linear_recurrence(A, b, x0, reverse=reverse)
+    At, bt = (A[:, ::-1], b[:, ::-1]) if reverse else (A, b)
+    M = np.zeros((n, T * S, T * S))
+    rhs = bt.copy()
+    rhs[:, 0] += np.einsum("nij,nj->ni", At[:, 0], x0)
+    for t in range(T):
+        M[:, t * S:(t + 1) * S, t * S:(t + 1) * S] = np.eye(S)
+        if t:
+            M[:, t * S:(t + 1) * S, (t - 1) * S:t * S] = -At[:, t]
+    ref = np.linalg.solve(M, rhs.reshape(n, -1)[..., None])[..., 0].reshape(n, T, S)
+    if reverse:
+        ref = ref[:, ::-1]
+    np.testing.assert_allclose(x, ref, rtol=0, atol=1e-10)
+    if not reverse:
+        np.testing.assert_allclose(deer.linear_recurrence(A, b), deer.solve_forward_substitution(A, b),
+                                   rtol=0, atol=1e-12)
