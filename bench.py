@@ -2,12 +2,16 @@
 
 One step = one whole Newton solve (residual + Jacobian + scan + update +
 on-device convergence test, iterated to max|r| < 1e-6 or 20 updates) over
-the full batch, with the projections already resident in HBM.
+the full batch, with the projections already resident in HBM.  For the
+forward + backward workload (--workload lstm_fwd_bwd) a step is the solve
+followed by the adjoint pass for upstream gradients dL/dh_t.
 
 Prints ONE JSON line: throughput in hidden-state elements per second
-(B*T*D per solve), the dominant kernel's achieved algorithmic HBM bandwidth
-against the MI355X peak, and the CPU oracle timed on a bounded sample of the
-same workload on the host cores.
+(B*T*D per solve); the dominant kernel's two roofs, algorithmic HBM bytes
+against the MI355X 8 TB/s and algorithmic VALU issue slots against the
+unpacked fp32 VALU rate, with `roofline` set to the one it runs closest to;
+and the CPU oracle timed on a bounded sample of the same workload on the
+host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gru_f32]
 """
@@ -22,7 +26,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-VALU_PEAK_TOPS = 39.32          # 256 CU x 4 SIMD x 16 lanes x 2.4 GHz, non-packed fp32 lane-ops
+# Unpacked fp32 VALU issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-ops/s
+# (the 157.3 TFLOP/s figure counts an FMA as two flops and packed fp32 as two
+# lanes; these kernels issue no packed fp32).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+# Algorithmic VALU issue slots per hidden-state element and Newton pass, from
+# the cell formulas: gate pre-activations, exp2/rcp gates (a transcendental
+# issues in two slots), residual, local Jacobian, one map composition, the
+# update and the residual max.  The last pass of a unit only evaluates the
+# residual.  ParaGRU: 26 ops + 6 transcendentals per update pass, 12 + 6 on
+# the final pass; ParaLSTM (2x2 maps): 52 + 10, and 18 + 10.
+VALU_SLOTS = {"gru": (26 + 2 * 6, 12 + 2 * 6), "lstm": (52 + 2 * 10, 18 + 2 * 10)}
 METRIC = "hidden-state elems/sec per Newton solve (B·T·D) + % of MI355X HBM peak"
 
 
@@ -31,6 +46,25 @@ def algorithmic_bytes(w):
     diagonal weights and the initial states, write every state once."""
     ub = 2 if w.u_dtype == "bf16" else 4
     return w.G * w.N * ub + w.G * w.D * 4 + w.S * w.B * w.D * 4 + w.S * w.N * 4
+
+
+def adjoint_bytes(w):
+    """Compulsory HBM traffic of one adjoint pass: read the projections, the
+    converged states and the upstream gradients dL/dh_t, write dL/du; the
+    [G][D] and [B][D] vectors (a, s0, da, ds0) are included."""
+    ub = 2 if w.u_dtype == "bf16" else 4
+    return (w.G * w.N * ub + w.S * w.N * 4 + w.N * 4 + w.G * w.N * 4
+            + 2 * w.G * w.D * 4 + 2 * w.S * w.B * w.D * 4)
+
+
+def data_recipe(w):
+    parts = [f"u~N(0,1) {'rounded to bf16' if w.u_dtype == 'bf16' else 'f32'}", "a~U(-1,1)",
+             f"s0~N(0,{w.s0_std}^2)" if w.s0_std else "s0=0"]
+    if w.f_bias:
+        parts.append(f"forget-gate bias +{w.f_bias:g}")
+    if w.adjoint:
+        parts.append("dL/dh_t~N(0,1)")
+    return f"synthetic (seeded numpy PCG64, seed {w.seed}: " + ", ".join(parts) + ")"
 
 
 def kernel_source_digest():
@@ -132,30 +166,66 @@ def main():
         return pr.solve_lstm(u, a, s0[0], s0[1], out=out, tol=w.tol, max_iters=w.max_iters,
                              info=info, stream=stream)[1]
 
+    adj_out = None
+    if w.adjoint:
+        gh = torch.from_numpy(inp.dh).to(dev)
+        gs = [None, gh] if w.cell == "lstm" else [gh]
+
+    def backward():
+        nonlocal adj_out
+        adj_out = pr.adjoint(w.cell, u, a, s0, out, gs, stream=stream, out=adj_out)
+
     # convergence report (untimed; the solve is deterministic)
     info = pr.read_info(solve(True))
     for _ in range(args.warmup):
         solve(False)
+        if w.adjoint:
+            backward()
     torch.cuda.synchronize()
 
-    # timed region: K solves; every launch bracketed by HIP events on its stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # timed region: K steps; every launch bracketed by HIP events on its stream
+    nev = 3 if w.adjoint else 2
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
+    for ev in evs:
+        ev[0].record(stream)
         solve(False)
-        e1.record(stream)
+        ev[1].record(stream)
+        if w.adjoint:
+            backward()
+            ev[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     ms_per_step = wall * 1e3 / args.steps
-    kavg_ms = sum(kern_ms) / len(kern_ms)
-    kmin_ms = min(kern_ms)
 
-    abytes = algorithmic_bytes(w)
-    achieved = abytes / (kavg_ms * 1e-3) / 1e9
+    def kernel_stats(i, name, nbytes):
+        ms = [ev[i].elapsed_time(ev[i + 1]) for ev in evs]
+        avg = sum(ms) / len(ms)
+        return {"kernel": name, "ms_avg": avg, "ms_min": min(ms), "bytes": nbytes,
+                "achieved": nbytes / (avg * 1e-3) / 1e9}
+
+    kernels = [kernel_stats(0, "newton_kernel", algorithmic_bytes(w))]
+    # VALU issue slots of the solve: every unit runs its updates plus one
+    # final residual pass (iters_mean = updates per unit)
+    upd, fin = VALU_SLOTS[w.cell]
+    kernels[0]["valu_ops"] = w.N * (info["iters_mean"] * upd + fin)
+    if w.adjoint:
+        kernels.append(kernel_stats(1, "adjoint_kernel", adjoint_bytes(w)))
+    dom = max(kernels, key=lambda k: k["ms_avg"])
+    abytes, kavg_ms, kmin_ms = dom["bytes"], dom["ms_avg"], dom["ms_min"]
+    hbm = {"achieved": dom["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": dom["achieved"] / HBM_PEAK_GBS}
+    valu = None
+    if "valu_ops" in dom:
+        tops = dom["valu_ops"] / (kavg_ms * 1e-3) / 1e12
+        valu = {"achieved": tops, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
+                "frac": tops / VALU_PEAK_TOPS, "ops_per_launch": dom["valu_ops"],
+                "ops": "algorithmic VALU lane-op issue slots (exp2/rcp = 2)"}
+    # the binding roof is the one the kernel runs closest to
+    bound = "alu" if valu is not None and valu["frac"] > hbm["frac"] else "hbm"
+    roof = valu if bound == "alu" else hbm
     traffic = measured_traffic(args.workload)
     K, W, nb = pr.plan(w.cell, pr.make_shape(w.B, w.T, w.D))
     line = {
@@ -170,18 +240,20 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16-in/f32" if w.u_dtype == "bf16" else "f32",
-        "data": "synthetic (seeded numpy PCG64: u~N(0,1), a~U(-1,1), h0~N(0,0.1^2))",
+        "data": data_recipe(w),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol,
                    "max_iters": w.max_iters, "seed": w.seed, "tiling": {"K": K, "W": W,
                    "time_blocks": nb}, "newton_updates": info["iters"],
                    "newton_updates_mean": info["iters_mean"], "converged": info["converged"],
                    "max_abs_res": info["max_abs_res"]},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+        "roofline": {"bound": bound, "achieved": roof["achieved"], "peak": roof["peak"],
+                     "unit": roof["unit"], "frac": roof["frac"],
                      "traffic": traffic, "algorithmic_bytes": abytes,
-                     "kernel": "newton_kernel", "kernel_ms_avg": kavg_ms,
-                     "kernel_ms_min": kmin_ms},
+                     "kernel": dom["kernel"], "kernel_ms_avg": kavg_ms,
+                     "kernel_ms_min": kmin_ms, "hbm": hbm, "valu": valu},
     }
+    if len(kernels) > 1:
+        line["kernels"] = kernels
     if args.copy_mib:
         n = args.copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

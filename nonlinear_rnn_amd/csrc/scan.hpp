@@ -50,7 +50,9 @@ __device__ __forceinline__ float max_abs(float m, float x)
 // library goes through it, so two places that apply the same map to the
 // same vector get the same bits.
 
-struct Map1 {  // diagonal Jacobian (ParaGRU): 1x1 per channel
+// 8-byte aligned so a map in LDS moves as one 64-bit access whose
+// immediate offset reaches every step's slot from one base address.
+struct alignas(8) Map1 {  // diagonal Jacobian (ParaGRU): 1x1 per channel
     float a, b;
 };
 __device__ __forceinline__ Map1 identity_map(Map1) { return {1.0f, 0.0f}; }

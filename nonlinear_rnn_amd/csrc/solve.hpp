@@ -44,6 +44,11 @@ constexpr int32_t kStopBase = 1 << 24;
 #ifndef PARARNN_GRU_MAPS_IN_LDS
 #define PARARNN_GRU_MAPS_IN_LDS 1
 #endif
+// Occupancy target (waves per SIMD) of the unmasked K = 16 ParaGRU loop with
+// up to 4 waves per workgroup: 4 (128 VGPRs) or 5 (96 VGPRs).
+#ifndef PARARNN_GRU_K16_WAVES
+#define PARARNN_GRU_K16_WAVES 4
+#endif
 
 struct SolveArgs {
     const void *u[4];
@@ -287,22 +292,25 @@ struct Slot {
 };
 
 // Where the lane's running compositions wait between up-sweep and down-sweep:
-// in VGPRs, or (ParaGRU: 2 floats per step) in LDS, which frees 2K VGPRs and
-// lets 4 workgroups share a CU.
-template <class Cell, int K, bool FULL>
+// in VGPRs, or (ParaGRU: 2 floats per step) in LDS, which frees 2K VGPRs.
+// The last step's composition is the lane aggregate itself and stays in
+// registers, so K - 1 steps go to LDS: 30 KB per 4-wave workgroup at K = 16,
+// which lets 5 such workgroups (5 waves per SIMD) share a CU's 160 KB.
+template <class Cell, int K, int W, bool FULL>
 struct MapStore {
     static constexpr bool kLds =
         PARARNN_GRU_MAPS_IN_LDS && sizeof(typename Cell::Map) == 8 && K >= 8;
-    // the unmasked ParaGRU loop then fits 4 waves per SIMD without spills
-    static constexpr int kMinWavesPerEu = (kLds && FULL && K <= 16) ? 4 : 1;
+    // register budget of the unmasked ParaGRU loop
+    static constexpr int kMinWavesPerEu =
+        !(kLds && FULL && K <= 16) ? 1 : (K == 16 && W <= 4) ? PARARNN_GRU_K16_WAVES : 4;
 };
 
 // LDS of the Newton loop: wave aggregates (double-buffered by iteration
-// parity) and, optionally, the running compositions.
+// parity) and, optionally, the running compositions of steps 0..K-2.
 template <class Cell, int K, int W, bool MAPS_LDS>
 struct LoopSmem {
     Slot<typename Cell::Map> slots[2][W];
-    typename Cell::Map mlds[MAPS_LDS ? K : 1][MAPS_LDS ? W * kWave : 1];
+    typename Cell::Map mlds[MAPS_LDS ? K - 1 : 1][MAPS_LDS ? W * kWave : 1];
 };
 
 // Lane's K steps of every gate, pre-scaled for the exp2-based gates.
@@ -365,10 +373,11 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             mxf = resmax(mxf, mk);
             prev = s[kk];
             agg = kk == 0 ? mk : compose(mk, agg);
-            if constexpr (MAPS_LDS)
-                sm.mlds[kk][threadIdx.x] = agg;
-            else
+            if constexpr (MAPS_LDS) {
+                if (kk < K - 1) sm.mlds[kk][threadIdx.x] = agg;
+            } else {
                 m[kk] = agg;
+            }
         }
         // ---- wave scan, then block exchange through LDS
         const M inc = wave_scan_inclusive(agg);
@@ -446,13 +455,13 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 // One work unit per workgroup.  Serves every case: several time blocks per
 // channel (dynamic tickets), ragged T, warm starts.
 template <class Cell, int K, int W, bool BF16, bool FULL>
-__global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, FULL>::kMinWavesPerEu))
+__global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWavesPerEu))
     newton_kernel(SolveArgs A)
 {
     using V = typename Cell::Vec;
     constexpr int G = Cell::G, S = Cell::S;
     constexpr int P = W * kWave * K;
-    constexpr bool kMapsLds = MapStore<Cell, K, FULL>::kLds;
+    constexpr bool kMapsLds = MapStore<Cell, K, W, FULL>::kLds;
 
     __shared__ LoopSmem<Cell, K, W, kMapsLds> sm;
     __shared__ int64_t s_ticket;

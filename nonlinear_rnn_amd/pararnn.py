@@ -245,11 +245,13 @@ def read_info(info_t) -> dict:
 
 
 def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
-            waves_per_block=0, workspace=None, stream=None):
+            waves_per_block=0, workspace=None, stream=None, out=None):
     """Backward pass of a converged solve for L = sum_t <gs_t, s_t>.
     cell "gru" (s0, s, gs: [h]) or "lstm" ([c, h]); an entry of gs may be
     None (zero).  Returns dict(du=[G planes], da [G][D], ds0=[S], lam=[S] or
-    None), all float32 device tensors."""
+    None), all float32 device tensors; `out`, a dict of that form returned by
+    an earlier call on the same shapes, is written in place instead of
+    allocating."""
     lib = load()
     cell = CELLS.get(cell, cell)
     G, S = N_GATES[cell], N_STATES[cell]
@@ -260,12 +262,30 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
     dev = u[0].device
     us = _strides(u, "u") or (D * T, T)
     ss = _strides(s + [g for g in gs if g is not None], "states") or (D * T, T)
-    du = [torch.empty_strided((B, D, T), (us[0], us[1], 1), dtype=torch.float32, device=dev)
-          for _ in range(G)]
-    da = torch.empty((G, D), dtype=torch.float32, device=dev)
-    ds0 = [torch.empty((B, D), dtype=torch.float32, device=dev) for _ in range(S)]
-    lam = ([torch.empty_strided((B, D, T), (ss[0], ss[1], 1), dtype=torch.float32, device=dev)
-            for _ in range(S)] if with_lambda else None)
+    if out is not None:
+        du, da, ds0, lam = list(out["du"]), out["da"], list(out["ds0"]), out.get("lam")
+        lam = list(lam) if (lam is not None and with_lambda) else None
+        dense = (D * T, T)
+        if (len(du) != G or len(ds0) != S or tuple(da.shape) != (G, D)
+                or any(tuple(x.shape) != (B, D, T) for x in du + (lam or []))
+                or (_strides(du, "du") or dense) != us
+                or any(tuple(x.shape) != (B, D) for x in ds0)
+                or (with_lambda and (lam is None or len(lam) != S
+                                     or (_strides(lam, "lam") or dense) != ss))):
+            raise ValueError("out buffers do not match this problem")
+        for x in du + [da] + ds0 + (lam or []):
+            if x.dtype != torch.float32 or x.device != dev:
+                raise ValueError("out buffers must be float32 on the device of u")
+        for x in [da] + ds0:
+            if not x.is_contiguous():
+                raise ValueError("da and ds0 outputs must be contiguous")
+    else:
+        du = [torch.empty_strided((B, D, T), (us[0], us[1], 1), dtype=torch.float32,
+                                  device=dev) for _ in range(G)]
+        da = torch.empty((G, D), dtype=torch.float32, device=dev)
+        ds0 = [torch.empty((B, D), dtype=torch.float32, device=dev) for _ in range(S)]
+        lam = ([torch.empty_strided((B, D, T), (ss[0], ss[1], 1), dtype=torch.float32,
+                                    device=dev) for _ in range(S)] if with_lambda else None)
     shape = make_shape(B, T, D, us, ss)
     newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
     nws = workspace_bytes(cell, shape, newton, adjoint=True)

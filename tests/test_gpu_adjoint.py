@@ -108,3 +108,28 @@ def test_adjoint_empty_time():
     torch.cuda.synchronize()
     assert float(out["da"].abs().max()) == 0.0
     assert float(out["ds0"][0].abs().max()) == 0.0
+
+
+def test_adjoint_writes_into_given_buffers():
+    """out= reuses the buffers of an earlier call (no allocation) and gives
+    the same result bit for bit; buffers of the wrong shape are refused."""
+    inp = make_inputs("lstm", 2, 700, 3, 631, f_bias=1.0, with_grad=True)
+    _, states, _, _ = bptt(inp)
+    u, a, s0 = dev_inputs(inp)
+    s = [torch.from_numpy(x.astype(np.float32)).to(DEV) for x in states]
+    gs = [None, torch.from_numpy(inp.dh).to(DEV)]
+    first = pr.adjoint("lstm", u, a, s0, s, gs, with_lambda=True)
+    ref = {k: [x.clone() for x in v] if isinstance(v, list) else v.clone()
+           for k, v in first.items()}
+    for v in first["du"] + first["ds0"] + first["lam"] + [first["da"]]:
+        v.fill_(7.0)
+    again = pr.adjoint("lstm", u, a, s0, s, gs, with_lambda=True, out=first)
+    torch.cuda.synchronize()
+    assert again["du"][0].data_ptr() == first["du"][0].data_ptr()
+    for k in ("du", "ds0", "lam"):
+        for x, y in zip(again[k], ref[k]):
+            assert torch.equal(x, y)
+    assert torch.equal(again["da"], ref["da"])
+    bad = dict(first, da=torch.empty((3, 3), device=DEV))
+    with pytest.raises(ValueError):
+        pr.adjoint("lstm", u, a, s0, s, gs, out=bad)
