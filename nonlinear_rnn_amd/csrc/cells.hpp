@@ -46,16 +46,33 @@ struct GruCell {
     }
     static __device__ __forceinline__ float uscale(int g) { return g == 2 ? -2.0f * kLog2e : -kLog2e; }
 
+    struct Gates {
+        float z, r, c;
+    };
+    static __device__ __forceinline__ Gates gates(const Coef &p, const float (&u)[G], float hp)
+    {
+        Gates q;
+        q.z = sigmoid_q(fmaf_(p.qz, hp, u[0]));
+        q.r = sigmoid_q(fmaf_(p.qr, hp, u[1]));
+        q.c = tanh_q(fmaf_(p.qc, q.r * hp, u[2]));
+        return q;
+    }
+    // -r_t = f(h_{t-1} = hp, u_t) - h_t alone (no Jacobian).
+    static __device__ __forceinline__ Vec1 step_residual(const Coef &p, const float (&u)[G],
+                                                         const Vec1 &hp_, const Vec1 &h_)
+    {
+        const float hp = hp_.x;
+        const Gates q = gates(p, u, hp);
+        return {fmaf_(q.z, q.c - hp, hp - h_.x)};
+    }
     // Affine map of one step at (h_{t-1} = hp, u_t) for the current iterate
     // h_t = h.  b = -r_t.
     static __device__ __forceinline__ Map1 step_map(const Coef &p, const float (&u)[G],
                                                     const Vec1 &hp_, const Vec1 &h_)
     {
         const float hp = hp_.x;
-        const float z = sigmoid_q(fmaf_(p.qz, hp, u[0]));
-        const float r = sigmoid_q(fmaf_(p.qr, hp, u[1]));
-        const float rh = r * hp;
-        const float c = tanh_q(fmaf_(p.qc, rh, u[2]));
+        const Gates q = gates(p, u, hp);
+        const float z = q.z, r = q.r, c = q.c;
         const float cmh = c - hp;
         const float b = fmaf_(z, cmh, hp - h_.x);   // f - h_t = -r_t, f = (1 - z) h + z c
         // df/dh = (1 - z) + z [ (c - h)(1 - z) a_z + (1 - c^2) a_c (r + h a_r r(1 - r)) ]
@@ -91,16 +108,34 @@ struct LstmCell {
     }
     static __device__ __forceinline__ float uscale(int g) { return g == 2 ? -2.0f * kLog2e : -kLog2e; }
 
+    struct Gates {
+        float i, f, g, o, c, tc;  // gates, c' and tanh(c')
+    };
+    static __device__ __forceinline__ Gates gates(const Coef &p, const float (&u)[G], float cp,
+                                                  float hp)
+    {
+        Gates q;
+        q.i = sigmoid_q(fmaf_(p.qi, hp, u[0]));
+        q.f = sigmoid_q(fmaf_(p.qf, hp, u[1]));
+        q.g = tanh_q(fmaf_(p.qg, hp, u[2]));
+        q.o = sigmoid_q(fmaf_(p.qo, hp, u[3]));
+        q.c = fmaf_(q.f, cp, q.i * q.g);
+        q.tc = tanh_q(q.c * (-2.0f * kLog2e));
+        return q;
+    }
+    // -r_t = f(s_{t-1} = sp, u_t) - s_t alone (no Jacobian).
+    static __device__ __forceinline__ Vec2 step_residual(const Coef &p, const float (&u)[G],
+                                                         const Vec2 &sp, const Vec2 &s)
+    {
+        const Gates q = gates(p, u, sp.x0, sp.x1);
+        return {q.c - s.x0, q.o * q.tc - s.x1};
+    }
     static __device__ __forceinline__ Map2 step_map(const Coef &p, const float (&u)[G],
                                                     const Vec2 &sp, const Vec2 &s)
     {
-        const float cp = sp.x0, hp = sp.x1;
-        const float i = sigmoid_q(fmaf_(p.qi, hp, u[0]));
-        const float f = sigmoid_q(fmaf_(p.qf, hp, u[1]));
-        const float g = tanh_q(fmaf_(p.qg, hp, u[2]));
-        const float o = sigmoid_q(fmaf_(p.qo, hp, u[3]));
-        const float c = fmaf_(f, cp, i * g);
-        const float tc = tanh_q(c * (-2.0f * kLog2e));
+        const float cp = sp.x0;
+        const Gates q = gates(p, u, cp, sp.x1);
+        const float i = q.i, f = q.f, g = q.g, o = q.o, c = q.c, tc = q.tc;
         const float h = o * tc;
         Map2 m;
         m.b0 = c - s.x0;

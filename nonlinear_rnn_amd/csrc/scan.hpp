@@ -71,6 +71,16 @@ __device__ __forceinline__ Map1 keep_or_identity(const Map1 &m, bool keep)
     return {keep ? m.a : 1.0f, keep ? m.b : 0.0f};
 }
 __device__ __forceinline__ Vec1 apply(const Map1 &m, const Vec1 &v) { return {fmaf_(m.a, v.x, m.b)}; }
+__device__ __forceinline__ float resmax(float mx, const Vec1 &r) { return max_abs(mx, r.x); }
+// The same value, but one the compiler cannot prove equal to its source
+// (an empty asm that claims to modify it).
+__device__ __forceinline__ float opaque(float x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ Vec1 opaque(const Vec1 &v) { return {opaque(v.x)}; }
+__device__ __forceinline__ Vec1 keep_or_zero(const Vec1 &v, bool keep) { return {keep ? v.x : 0.0f}; }
 
 struct Map2 {  // 2x2 block Jacobian (ParaLSTM), state order (c, h)
     float a00, a01, a10, a11, b0, b1;
@@ -103,6 +113,15 @@ __device__ __forceinline__ Vec2 apply(const Map2 &m, const Vec2 &v)
 {
     return {fmaf_(m.a00, v.x0, fmaf_(m.a01, v.x1, m.b0)),
             fmaf_(m.a10, v.x0, fmaf_(m.a11, v.x1, m.b1))};
+}
+__device__ __forceinline__ float resmax(float mx, const Vec2 &r)
+{
+    return max_abs(max_abs(mx, r.x0), r.x1);
+}
+__device__ __forceinline__ Vec2 opaque(const Vec2 &v) { return {opaque(v.x0), opaque(v.x1)}; }
+__device__ __forceinline__ Vec2 keep_or_zero(const Vec2 &v, bool keep)
+{
+    return {keep ? v.x0 : 0.0f, keep ? v.x1 : 0.0f};
 }
 
 // ------------------------------------------------------------ DPP moves ---

@@ -301,8 +301,10 @@ struct MapStore {
     static constexpr bool kLds =
         PARARNN_GRU_MAPS_IN_LDS && sizeof(typename Cell::Map) == 8 && K >= 8;
     // register budget of the unmasked ParaGRU loop
+    // (ParaLSTM: at most 256 VGPRs, two waves per SIMD)
     static constexpr int kMinWavesPerEu =
-        !(kLds && FULL && K <= 16) ? 1 : (K == 16 && W <= 4) ? PARARNN_GRU_K16_WAVES : 4;
+        !(kLds && FULL && K <= 16) ? (FULL ? 2 : 1)
+                                   : (K == 16 && W <= 4) ? PARARNN_GRU_K16_WAVES : 4;
 };
 
 // LDS of the Newton loop: wave aggregates (double-buffered by iteration
@@ -356,10 +358,42 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     const bool full = FULL || tb0 + P <= T;  // uniform over the workgroup
 
     const uint32_t tolb = __float_as_uint(A.tol);
+    // Newton converges quadratically: once max|r| < sqrt(tol) the next
+    // residual is expected below tol, so that evaluation skips the Jacobian
+    // and the scan.  A wrong guess only costs a second evaluation of the same
+    // iterate.  (Whole channels only: a time block must publish its map.)
+    const uint32_t predb = multi ? 0u : __float_as_uint(__builtin_sqrtf(A.tol));
     M m[MAPS_LDS ? 1 : K];  // running composition of the lane's steps 0..kk
     int32_t it = 0;
     uint32_t bmx = 0;
+    bool ronly = false;  // this evaluation is the predicted last one
+    int xp = 0;          // LDS exchange slot parity (alternates every exchange)
     for (;; ++it) {
+        if (ronly) {
+            // ---- predicted last evaluation: residual and its maximum only
+            // The states pass through an empty asm: otherwise the compiler
+            // sees that a wrong guess re-evaluates the same gates and keeps
+            // all K steps' gate values live for the full evaluation.
+            float mxf = 0.0f;
+            V prev = opaque(hin);
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) {
+                const V sk = opaque(s[kk]);
+                V rk = Cell::step_residual(cf, u[kk], prev, sk);
+                if (!full) rk = keep_or_zero(rk, t0 + kk < T);
+                mxf = resmax(mxf, rk);
+                prev = sk;
+            }
+            const uint32_t wmx = wave_max_to_last(__float_as_uint(mxf));
+            if (lane == kWave - 1) sm.slots[xp][wave].mx = wmx;
+            __syncthreads();
+            bmx = sm.slots[xp][0].mx;
+#pragma unroll
+            for (int j = 1; j < W; ++j) bmx = max(bmx, sm.slots[xp][j].mx);
+            xp ^= 1;
+            if (bmx < tolb || it == A.cap) break;
+            ronly = false;  // not yet: full evaluation of the same iterate
+        }
         // ---- residual, Jacobian and lane up-sweep.  Blocks that lie wholly
         // inside [0, T) take a path without per-step masks; the ragged last
         // block turns steps past T into identity maps by selection.
@@ -384,7 +418,8 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         const M exc = wave_shift_up(inc);
         // |r| bit patterns: unsigned order = float order, NaN above +inf
         const uint32_t wmx = wave_max_to_last(__float_as_uint(mxf));
-        const int par = it & 1;
+        const int par = xp;
+        xp ^= 1;
         if (lane == kWave - 1) {
             sm.slots[par][wave].agg = inc;
             sm.slots[par][wave].mx = wmx;
@@ -411,6 +446,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             if (multi && threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
             break;
         }
+        ronly = bmx < predb;
         // ---- down-sweep from the carries, Newton update
         V dw = din;
 #pragma unroll
