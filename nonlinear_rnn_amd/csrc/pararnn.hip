@@ -96,13 +96,13 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
         }
         if (K == 0) K = tab[pick][0];
         if (W == 0) W = tab[pick][1];
-        // Past one workgroup per channel, GRU time blocks of 2 waves x 32
-        // steps per lane (the same 4096 steps) need half the cross-block
-        // exchanges per step of the 4-wave layout.
-        if (!adjoint && cell == PARARNN_GRU && opt_k_w_unset(opt) &&
+        // Past 4096 steps a ParaGRU channel takes 8-wave time blocks of 8192
+        // steps: half the cross-block exchanges per step of 4096-step blocks,
+        // still 4 waves per SIMD (106 VGPRs, 61 KB LDS per workgroup).
+        if (kind == 0 && cell == PARARNN_GRU && opt_k_w_unset(opt) &&
             sh->T > (int64_t)kWave * tab[0][0] * tab[0][1]) {
-            K = 32;
-            W = 2;
+            K = 16;
+            W = 8;
         }
     }
     const bool lstm = cell == PARARNN_LSTM;

@@ -42,7 +42,7 @@ def test_status_strings():
 def test_plan_defaults():
     # one workgroup per channel up to 4096 steps, then time blocks
     assert pr.plan("gru", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
-    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (32, 2, 4)
+    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (16, 8, 2)
     assert pr.plan("gru", pr.make_shape(1, 1024, 64)) == (16, 1, 1)
     assert pr.plan("gru", pr.make_shape(1, 1, 64)) == (1, 1, 1)
     assert pr.plan("lstm", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
@@ -74,7 +74,7 @@ def test_workspace_sizes():
     n = pr.make_newton(1e-6, 20)
     assert pr.workspace_bytes("gru", pr.make_shape(8, 4096, 1024), n) == 0
     ws = pr.workspace_bytes("gru", pr.make_shape(4, 16384, 4096), n)
-    units = 4 * 4096 * 4
+    units = 4 * 4096 * 2  # two 8192-step blocks per channel
     assert ws >= units * 4 + units * 21 * 4 * 4
     ws2 = pr.workspace_bytes("gru", pr.make_shape(4, 16384, 4096), pr.make_newton(1e-6, 20,
                              init_from_output=True))

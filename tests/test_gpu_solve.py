@@ -204,3 +204,18 @@ def test_many_channels(cell, dtype, T, KW):
     bs = [c[0] for c in chans]
     ds = [c[1] for c in chans]
     assert max_err([g[bs, ds] for g in got], ref) < TOL32
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_long_sequence_default_tiling(cell):
+    """Past 4096 steps: the default time blocks (ParaGRU 8192 steps, ParaLSTM
+    4096), a ragged last block, bf16 and float32 projections."""
+    from nonlinear_rnn_amd import pararnn as pr
+    T = 17001
+    K, W, nb = pr.plan(cell, pr.make_shape(2, T, 2))
+    assert nb == -(-T // (64 * K * W)) and nb >= 3
+    for dt in ("f32", "bf16"):
+        inp = make_inputs(cell, 2, T, 2, 1700 + len(dt), u_dtype=dt, f_bias=1.0)
+        got, info = gpu_solve(inp, 1e-6, 30)
+        assert info["converged"] and info["units"] == 4 * nb
+        assert max_err(got, oracle_states(inp, rounded=True)) < TOL32
