@@ -254,6 +254,23 @@ def main():
     }
     if len(kernels) > 1:
         line["kernels"] = kernels
+    # context: the same trajectory by step-by-step application on the GPU
+    # (one lane per channel), the baseline of the pages' parallel speed-up
+    seq_out = [torch.empty_like(x) for x in out]
+    for _ in range(2):
+        pr.sequential(w.cell, u, a, s0, out=seq_out, stream=stream)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(5)]
+    for e0, e1 in sev:
+        e0.record(stream)
+        pr.sequential(w.cell, u, a, s0, out=seq_out, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    seq_ms = sorted(e0.elapsed_time(e1) for e0, e1 in sev)[len(sev) // 2]
+    line["gpu_sequential"] = {"value": w.N / (seq_ms * 1e-3), "unit": "elem/s", "ms": seq_ms,
+                              "newton_kernel_speedup": seq_ms / kernels[0]["ms_avg"],
+                              "kind": "step-by-step application, one lane per channel"}
+    del seq_out
     if args.copy_mib:
         n = args.copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -186,6 +186,27 @@ pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
                               const pararnn_newton_t *opt, void *ws, size_t ws_bytes,
                               void *stream);
 
+/*
+ * Step-by-step application of the recurrence, one lane per channel:
+ * s_t = f(s_{t-1}, u_t) for t = 1..T from the given s_0 — the sequential
+ * evaluation whose result the Newton solve reaches ("Параллельность RNN?",
+ * forpes.ru, §1.1: the trajectory is the unique zero of the residual) and
+ * the baseline of the pages' parallel-vs-sequential speed-up (voguetech.ru
+ * ParaRNN article, "Что именно сделали технически").  Its time is T times
+ * one step's dependency-chain latency, nearly independent of the number of
+ * channels until they fill the device, so for many channels and moderate T
+ * it can beat the Newton solve; for few channels and long T it cannot.
+ *   cell, shape, u, u_dtype, a : as for pararnn_solve_gru / _lstm
+ *   s0 : S pointers to [B][D] initial states (LSTM order c, h)
+ *   s  : S pointers to [B][D][T] float32 outputs (s_stride_*)
+ * Same conventions: device pointers, caller's stream, no allocation, no
+ * workspace, arguments checked before any HIP call.
+ */
+pararnn_status_t pararnn_sequential(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                                    const void *const *u, pararnn_dtype_t u_dtype,
+                                    const float *a, const float *const *s0, float *const *s,
+                                    void *stream);
+
 /* Static description of a status code. */
 const char *pararnn_status_string(pararnn_status_t status);
 

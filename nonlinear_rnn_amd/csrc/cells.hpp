@@ -57,6 +57,13 @@ struct GruCell {
         q.c = tanh_q(fmaf_(p.qc, q.r * hp, u[2]));
         return q;
     }
+    // f(h_{t-1} = hp, u_t): one step of the recurrence.
+    static __device__ __forceinline__ Vec1 next(const Coef &p, const float (&u)[G], const Vec1 &hp_)
+    {
+        const float hp = hp_.x;
+        const Gates q = gates(p, u, hp);
+        return {fmaf_(q.z, q.c - hp, hp)};
+    }
     // -r_t = f(h_{t-1} = hp, u_t) - h_t alone (no Jacobian).
     static __device__ __forceinline__ Vec1 step_residual(const Coef &p, const float (&u)[G],
                                                          const Vec1 &hp_, const Vec1 &h_)
@@ -122,6 +129,12 @@ struct LstmCell {
         q.c = fmaf_(q.f, cp, q.i * q.g);
         q.tc = tanh_q(q.c * (-2.0f * kLog2e));
         return q;
+    }
+    // f(s_{t-1} = sp, u_t): one step of the recurrence.
+    static __device__ __forceinline__ Vec2 next(const Coef &p, const float (&u)[G], const Vec2 &sp)
+    {
+        const Gates q = gates(p, u, sp.x0, sp.x1);
+        return {q.c, q.o * q.tc};
     }
     // -r_t = f(s_{t-1} = sp, u_t) - s_t alone (no Jacobian).
     static __device__ __forceinline__ Vec2 step_residual(const Coef &p, const float (&u)[G],

@@ -7,6 +7,7 @@
 
 #include "adjoint.hpp"
 #include "scan_kernel.hpp"
+#include "sequential.hpp"
 #include "solve.hpp"
 
 namespace pararnn {
@@ -34,6 +35,9 @@ PARARNN_DECLARE_LAUNCHERS(gru_bf16)
 PARARNN_DECLARE_LAUNCHERS(lstm_f32)
 PARARNN_DECLARE_LAUNCHERS(lstm_bf16)
 #undef PARARNN_DECLARE_LAUNCHERS
+
+// Step-by-step application, one lane per channel.
+hipError_t launch_sequential(bool lstm, bool bf16, hipStream_t st, const SeqArgs &a);
 
 // Standalone scan: state size 1 or 2, forward or reverse.
 hipError_t launch_scan(int S, int K, int W, bool reverse, int64_t groups, hipStream_t st,

@@ -361,6 +361,52 @@ pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
                                                                                   : PARARNN_ERR_HIP;
 }
 
+pararnn_status_t pararnn_sequential(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                                    const void *const *u, pararnn_dtype_t u_dtype,
+                                    const float *a, const float *const *s0, float *const *s,
+                                    void *stream)
+{
+    if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return PARARNN_ERR_INVALID;
+    pararnn_status_t st = check_shape(shape);
+    if (st != PARARNN_OK) return st;
+    if (u_dtype != PARARNN_F32 && u_dtype != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;
+    const int G = cell_G(cell), S = cell_S(cell);
+    const int64_t channels = shape->B * shape->D;
+    if (channels == 0 || shape->T == 0) return PARARNN_OK;
+    if ((channels + kWave - 1) / kWave >= (int64_t(1) << 31)) return PARARNN_ERR_UNSUPPORTED;
+    if (!u || !a || !s0 || !s) return PARARNN_ERR_INVALID;
+    for (int g = 0; g < G; ++g)
+        if (!u[g]) return PARARNN_ERR_INVALID;
+    for (int c = 0; c < S; ++c)
+        if (!s0[c] || !s[c]) return PARARNN_ERR_INVALID;
+    SeqArgs A;
+    std::memset(&A, 0, sizeof(A));
+    for (int g = 0; g < G; ++g) A.u[g] = u[g];
+    A.a = a;
+    for (int c = 0; c < S; ++c) {
+        A.s0[c] = s0[c];
+        A.s[c] = s[c];
+    }
+    A.T = shape->T;
+    A.D = shape->D;
+    A.usb = shape->u_stride_b;
+    A.usd = shape->u_stride_d;
+    A.ssb = shape->s_stride_b;
+    A.ssd = shape->s_stride_d;
+    A.channels = channels;
+    const int ve = u_dtype == PARARNN_BF16 ? 8 : 4;
+    bool uv = (shape->T % ve == 0) && (shape->u_stride_b % ve == 0) &&
+              (shape->u_stride_d % ve == 0);
+    for (int g = 0; g < G; ++g) uv = uv && aligned16(u[g]);
+    bool sv = (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) && (shape->s_stride_d % 4 == 0);
+    for (int c = 0; c < S; ++c) sv = sv && aligned16(s[c]);
+    A.u_vec = uv ? 1 : 0;
+    A.s_vec = sv ? 1 : 0;
+    const hipError_t e = launch_sequential(cell == PARARNN_LSTM, u_dtype == PARARNN_BF16,
+                                           static_cast<hipStream_t>(stream), A);
+    return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+}
+
 const char *pararnn_status_string(pararnn_status_t s)
 {
     switch (s) {

@@ -71,6 +71,8 @@ def load():
     lib.pararnn_solve_lstm.restype = i32
     lib.pararnn_solve_lstm.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, P(Newton), vp,
                                        vp, sz, vp]
+    lib.pararnn_sequential.restype = i32
+    lib.pararnn_sequential.argtypes = [i32, P(Shape), vp, i32, vp, vp, vp, vp]
     lib.pararnn_scan_workspace_bytes.restype = sz
     lib.pararnn_scan_workspace_bytes.argtypes = [i32, P(Shape), P(Newton)]
     lib.pararnn_scan.restype = i32
@@ -297,6 +299,35 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
                                ctypes.byref(newton), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream_handle(stream)))
     return dict(du=du, da=da, ds0=ds0, lam=lam)
+
+
+def sequential(cell, u, a, s0, *, out=None, stream=None):
+    """Step-by-step application s_t = f(s_{t-1}, u_t), one lane per channel
+    (no Newton iteration).  cell "gru" (s0: [h0]) or "lstm" ([c0, h0]); u as
+    for the solves.  Returns the S state planes [B][D][T] (float32)."""
+    lib = load()
+    cell = CELLS.get(cell, cell)
+    G, S = N_GATES[cell], N_STATES[cell]
+    u, s0 = list(u), list(s0)
+    if len(u) != G or len(s0) != S:
+        raise ValueError("wrong number of gate or state planes")
+    B, D, T = u[0].shape
+    dev = u[0].device
+    us = _strides(u, "u") or (D * T, T)
+    if out is None:
+        out = [torch.empty((B, D, T), dtype=torch.float32, device=dev) for _ in range(S)]
+    out = list(out)
+    if len(out) != S or any(tuple(x.shape) != (B, D, T) or x.dtype != torch.float32
+                            for x in out):
+        raise ValueError("out must be S float32 planes [B][D][T]")
+    ss = _strides(out, "states") or (D * T, T)
+    for x in s0:
+        if tuple(x.shape) != (B, D) or not x.is_contiguous() or x.dtype != torch.float32:
+            raise ValueError("initial states must be contiguous float32 [B][D]")
+    shape = make_shape(B, T, D, us, ss)
+    _check(lib.pararnn_sequential(cell, ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a),
+                                  _ptr_array(s0), _ptr_array(out), _stream_handle(stream)))
+    return out
 
 
 def scan(A, b, x0=None, *, reverse=False, out=None, steps_per_lane=0, waves_per_block=0,

@@ -150,3 +150,22 @@ def test_lstm_and_adjoint_reject_bad_arguments():
                                None, None, 0, None) == 3
     assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, None, s2, s2, s2, u, 1, s2, None,
                                None, None, 0, None) == 1
+
+
+def test_sequential_rejects_bad_arguments_before_any_device_call():
+    lib = pr.load()
+    sh = pr.make_shape(2, 16, 3)
+    one = ctypes.c_void_p(16)
+    u = (ctypes.c_void_p * 4)(one, one, one, one)
+    s = (ctypes.c_void_p * 2)(one, one)
+    assert lib.pararnn_sequential(7, ctypes.byref(sh), u, 0, one, s, s, None) == 1
+    assert lib.pararnn_sequential(0, None, u, 0, one, s, s, None) == 1
+    assert lib.pararnn_sequential(0, ctypes.byref(sh), u, 5, one, s, s, None) == 2
+    assert lib.pararnn_sequential(0, ctypes.byref(sh), None, 0, one, s, s, None) == 1
+    assert lib.pararnn_sequential(1, ctypes.byref(sh), u, 0, None, s, s, None) == 1
+    nul = (ctypes.c_void_p * 2)(one, None)
+    assert lib.pararnn_sequential(1, ctypes.byref(sh), u, 0, one, s, nul, None) == 1
+    bad = pr.make_shape(2, 16, 3, (10, 16), (48, 16))  # overlapping rows
+    assert lib.pararnn_sequential(0, ctypes.byref(bad), u, 0, one, s, s, None) == 1
+    empty = pr.make_shape(0, 16, 3)
+    assert lib.pararnn_sequential(0, ctypes.byref(empty), None, 0, None, None, None, None) == 0
