@@ -26,7 +26,7 @@ inline bool adjoint_tiling_built(bool, int K, int W)
 }
 
 #define PARARNN_DECLARE_LAUNCHERS(NAME)                                                          \
-    hipError_t launch_newton_##NAME(int K, int W, bool full, int64_t groups, hipStream_t st,    \
+    hipError_t launch_newton_##NAME(int K, int W, int variant, int64_t groups, hipStream_t st,  \
                                     const SolveArgs &a);                                        \
     hipError_t launch_adjoint_##NAME(int K, int W, int64_t groups, hipStream_t st,              \
                                      const AdjArgs &a);
@@ -47,12 +47,21 @@ hipError_t launch_scan(int S, int K, int W, bool reverse, int64_t groups, hipStr
     X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) X(4, 1) X(4, 2) X(4, 4)    \
         X(4, 8) X(8, 1) X(8, 2) X(8, 4) X(8, 8) X(16, 1) X(16, 2) X(16, 4) X(16, 8)
 
+// Newton kernel variants: 0 = any block (ragged T), 1 = blocks wholly inside
+// [0, T), 2 = as 1 with one block per channel (no cross-block code).
+enum { kNewtonAny = 0, kNewtonFull = 1, kNewtonFullSingle = 2 };
+
 #define PARARNN_NEWTON_CASE(CELL, BF16, KK, WW)                                                 \
     case KK * 100 + WW:                                                                         \
-        if (full)                                                                               \
-            hipLaunchKernelGGL((newton_kernel<CELL, KK, WW, BF16, true>), grid, block, 0, st, a); \
+        if (variant == kNewtonFullSingle)                                                       \
+            hipLaunchKernelGGL((newton_kernel<CELL, KK, WW, BF16, true, true>), grid, block, 0,  \
+                               st, a);                                                          \
+        else if (variant == kNewtonFull)                                                        \
+            hipLaunchKernelGGL((newton_kernel<CELL, KK, WW, BF16, true, false>), grid, block, 0, \
+                               st, a);                                                          \
         else                                                                                    \
-            hipLaunchKernelGGL((newton_kernel<CELL, KK, WW, BF16, false>), grid, block, 0, st, a); \
+            hipLaunchKernelGGL((newton_kernel<CELL, KK, WW, BF16, false, false>), grid, block,  \
+                               0, st, a);                                                       \
         break;
 
 #define PARARNN_ADJOINT_CASE(CELL, BF16, KK, WW)                                                \
@@ -62,7 +71,7 @@ hipError_t launch_scan(int S, int K, int W, bool reverse, int64_t groups, hipStr
 
 // EXTRA(X) lists tilings beyond the base set for this cell.
 #define PARARNN_DEFINE_LAUNCHERS(NAME, CELL, BF16, EXTRA)                                  \
-    hipError_t launch_newton_##NAME(int K, int W, bool full, int64_t groups, hipStream_t st,    \
+    hipError_t launch_newton_##NAME(int K, int W, int variant, int64_t groups, hipStream_t st,  \
                                     const SolveArgs &a)                                         \
     {                                                                                           \
         const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \

@@ -198,6 +198,7 @@ pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, co
     A.ssd = sh->s_stride_d;
     A.channels = pl.channels;
     A.tol = opt->tol;
+    A.guess_tol = std::sqrt(opt->tol);
     A.cap = opt->max_iters;
     A.nb = (int32_t)pl.nb;
     A.init_from_output = opt->init_from_output;
@@ -228,14 +229,16 @@ pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, co
     }
     if (!work) return PARARNN_OK;
     const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
-    const bool full = sh->T % pl.P == 0;
+    const int variant = sh->T % pl.P != 0 ? kNewtonAny
+                        : pl.nb == 1      ? kNewtonFullSingle
+                                          : kNewtonFull;
     hipError_t e;
     if (cell == PARARNN_GRU)
-        e = dt == PARARNN_BF16 ? launch_newton_gru_bf16(pl.K, pl.W, full, groups, strm, A)
-                               : launch_newton_gru_f32(pl.K, pl.W, full, groups, strm, A);
+        e = dt == PARARNN_BF16 ? launch_newton_gru_bf16(pl.K, pl.W, variant, groups, strm, A)
+                               : launch_newton_gru_f32(pl.K, pl.W, variant, groups, strm, A);
     else
-        e = dt == PARARNN_BF16 ? launch_newton_lstm_bf16(pl.K, pl.W, full, groups, strm, A)
-                               : launch_newton_lstm_f32(pl.K, pl.W, full, groups, strm, A);
+        e = dt == PARARNN_BF16 ? launch_newton_lstm_bf16(pl.K, pl.W, variant, groups, strm, A)
+                               : launch_newton_lstm_f32(pl.K, pl.W, variant, groups, strm, A);
     return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
 }
 

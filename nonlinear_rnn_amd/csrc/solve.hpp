@@ -59,6 +59,7 @@ struct SolveArgs {
     int64_t usb, usd, ssb, ssd;
     int64_t channels;
     float tol;
+    float guess_tol;  // max|r| below which the next evaluation is guessed to be the last (0 = never)
     int32_t cap;
     int32_t nb;
     int32_t init_from_output;
@@ -301,10 +302,10 @@ struct MapStore {
     static constexpr bool kLds =
         PARARNN_GRU_MAPS_IN_LDS && sizeof(typename Cell::Map) == 8 && K >= 8;
     // register budget of the unmasked ParaGRU loop
-    // (ParaLSTM: at most 256 VGPRs, two waves per SIMD)
+    // (everything else, ParaLSTM included: at most 256 VGPRs, two waves per
+    // SIMD; one more register would halve the occupancy)
     static constexpr int kMinWavesPerEu =
-        !(kLds && FULL && K <= 16) ? (FULL ? 2 : 1)
-                                   : (K == 16 && W <= 4) ? PARARNN_GRU_K16_WAVES : 4;
+        !(kLds && FULL && K <= 16) ? 2 : (K == 16 && W <= 4) ? PARARNN_GRU_K16_WAVES : 4;
 };
 
 // LDS of the Newton loop: wave aggregates (double-buffered by iteration
@@ -334,7 +335,7 @@ __device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uof
 // from the lane's pre-scaled projections `u`, its copy `hin` of the state
 // before its first step and the Newton start `s`; writes the converged states
 // and folds the unit into the info record.
-template <class Cell, int K, int W, bool FULL, bool MAPS_LDS>
+template <class Cell, int K, int W, bool FULL, bool MAPS_LDS, bool SINGLE>
 __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32_t k,
                                            const typename Cell::Coef &cf,
                                            const float (&u)[K][Cell::G],
@@ -353,16 +354,17 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     const int64_t T = A.T;
     const int64_t tb0 = (int64_t)k * P;
     const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
-    const bool multi = A.nb > 1;
+    const bool multi = !SINGLE && A.nb > 1;
     const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
     const bool full = FULL || tb0 + P <= T;  // uniform over the workgroup
 
     const uint32_t tolb = __float_as_uint(A.tol);
-    // Newton converges quadratically: once max|r| < sqrt(tol) the next
-    // residual is expected below tol, so that evaluation skips the Jacobian
-    // and the scan.  A wrong guess only costs a second evaluation of the same
-    // iterate.  (Whole channels only: a time block must publish its map.)
-    const uint32_t predb = multi ? 0u : __float_as_uint(__builtin_sqrtf(A.tol));
+    // Newton converges quadratically: once max|r| < sqrt(tol) (A.guess_tol)
+    // the next residual is expected below tol, so that evaluation skips the
+    // Jacobian and the scan.  A wrong guess only costs a second evaluation of
+    // the same iterate.  (Whole channels only: a time block must publish its
+    // map.)
+    const uint32_t predb = multi ? 0u : __float_as_uint(A.guess_tol);
     M m[MAPS_LDS ? 1 : K];  // running composition of the lane's steps 0..kk
     int32_t it = 0;
     uint32_t bmx = 0;
@@ -371,18 +373,17 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     for (;; ++it) {
         if (ronly) {
             // ---- predicted last evaluation: residual and its maximum only
-            // The states pass through an empty asm: otherwise the compiler
-            // sees that a wrong guess re-evaluates the same gates and keeps
-            // all K steps' gate values live for the full evaluation.
+            // The previous states pass through an empty asm: otherwise the
+            // compiler sees that a wrong guess re-evaluates the same gates
+            // and keeps all K steps' gate values live for the full evaluation.
             float mxf = 0.0f;
             V prev = opaque(hin);
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) {
-                const V sk = opaque(s[kk]);
-                V rk = Cell::step_residual(cf, u[kk], prev, sk);
+                V rk = Cell::step_residual(cf, u[kk], prev, s[kk]);
                 if (!full) rk = keep_or_zero(rk, t0 + kk < T);
                 mxf = resmax(mxf, rk);
-                prev = sk;
+                prev = opaque(s[kk]);
             }
             const uint32_t wmx = wave_max_to_last(__float_as_uint(mxf));
             if (lane == kWave - 1) sm.slots[xp][wave].mx = wmx;
@@ -490,7 +491,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 
 // One work unit per workgroup.  Serves every case: several time blocks per
 // channel (dynamic tickets), ragged T, warm starts.
-template <class Cell, int K, int W, bool BF16, bool FULL>
+template <class Cell, int K, int W, bool BF16, bool FULL, bool SINGLE>
 __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWavesPerEu))
     newton_kernel(SolveArgs A)
 {
@@ -507,7 +508,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
 
     int64_t ch;
     int32_t k;
-    if (A.nb > 1) {
+    if (!SINGLE && A.nb > 1) {
         if (threadIdx.x == 0) s_ticket = (int64_t)atomicAdd(A.ticket, 1u);
         __syncthreads();
         ticket_to_unit(s_ticket, A.nb, ch, k);
@@ -557,7 +558,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
             for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
         }
     }
-    solve_unit<Cell, K, W, FULL, kMapsLds>(A, ch, k, cf, u, s, hin, sm);
+    solve_unit<Cell, K, W, FULL, kMapsLds, SINGLE>(A, ch, k, cf, u, s, hin, sm);
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit
