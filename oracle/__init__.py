@@ -12,6 +12,8 @@ and this package imports nothing from it.
   derive it (residual, block-bidiagonal Jacobian, forward substitution, or a
   pairwise tree scan of affine maps), in numpy float64, for invariant and
   per-iteration checks.
+* ``oracle.projection`` — the input projection u = W x + b per batch row in
+  float64.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` against library routines (torch.nn.GRUCell /

@@ -436,3 +436,42 @@ def test_linear_recurrence_is_dense_solve(S, reverse, T):
     if not reverse:
         np.testing.assert_allclose(deer.linear_recurrence(A, b), deer.solve_forward_substitution(A, b),
                                    rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ projection ----
+
+def test_projection_matches_brute_force_loops():
+    from oracle import projection
+    rng = np.random.default_rng(71)
+    B, T, I, M = 2, 5, 4, 3
+    x = rng.standard_normal((B, T, I))
+    W = rng.standard_normal((M, I))
+    bias = rng.standard_normal(M)
+    u = projection.project(x, W, bias)
+    for b in range(B):
+        for m in range(M):
+            for t in range(T):
+                acc = bias[m]
+                for k in range(I):
+                    acc += W[m, k] * x[b, t, k]
+                assert abs(u[b, m, t] - acc) < 1e-12
+
+
+def test_projection_identity_weight_is_the_transpose():
+    from oracle import projection
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((3, 7, 6))
+    u = projection.project(x, np.eye(6))
+    assert u.shape == (3, 6, 7)
+    assert np.array_equal(u, np.transpose(x, (0, 2, 1)))
+
+
+def test_projection_bias_only_and_abs_scale():
+    from oracle import projection
+    bias = np.array([1.5, -2.0])
+    u = projection.project(np.zeros((1, 4, 3)), np.ones((2, 3)), bias)
+    assert np.array_equal(u, np.broadcast_to(bias[None, :, None], (1, 2, 4)))
+    x = np.array([[[1.0, -2.0]]])
+    W = np.array([[3.0, 4.0]])
+    assert projection.project(x, W)[0, 0, 0] == -5.0
+    assert projection.project_abs(x, W, np.array([-1.0]))[0, 0, 0] == 12.0
