@@ -207,6 +207,36 @@ pararnn_status_t pararnn_sequential(pararnn_cell_t cell, const pararnn_shape_t *
                                     const float *a, const float *const *s0, float *const *s,
                                     void *stream);
 
+/*
+ * Input projection: u = W x + b for every time step, the dense product that
+ * precedes the recurrence (the cells take u_t = W x_t + b as precomputed
+ * projections: voguetech.ru ParaRNN article, "Что именно сделали
+ * технически", item 3).  Per batch row b:
+ *     u[b][m][t] = sum_k W[m][k] x[b][t][k] + bias[m],  m < M, t < T, k < I
+ * Written channel-major with time contiguous, so for M = G*D the rows of
+ * gate g form that gate's [B][D][T] plane for the solves (plane g starts at
+ * u + g*D*u_stride_m; u_stride_b, u_stride_m are its strides).
+ *   x    : bfloat16, x[b][t][k] at b*x_stride_b + t*x_stride_t + k
+ *   w    : bfloat16, W[m][k] at m*w_stride_m + k
+ *   bias : float32 [M], or NULL (no bias)
+ *   u    : u_dtype (PARARNN_F32, or PARARNN_BF16 rounded to nearest even),
+ *          u[b][m][t] at b*u_stride_b + m*u_stride_m + t
+ * Products of bf16 values are exact in fp32 and accumulate in fp32 on the
+ * matrix cores.  Device pointers, caller's stream, no allocation; arguments
+ * checked before any HIP call (sizes >= 0, strides large enough that rows
+ * do not overlap).
+ */
+typedef struct {
+    int64_t B, T, I, M;
+    int64_t x_stride_b, x_stride_t;
+    int64_t w_stride_m;
+    int64_t u_stride_b, u_stride_m;
+} pararnn_proj_shape_t;
+
+pararnn_status_t pararnn_project(const pararnn_proj_shape_t *shape, const void *x,
+                                 const void *w, const float *bias, void *u,
+                                 pararnn_dtype_t u_dtype, void *stream);
+
 /* Static description of a status code. */
 const char *pararnn_status_string(pararnn_status_t status);
 

@@ -35,7 +35,8 @@ def compile_flags():
 
 
 SOURCES = ["pararnn.hip", "inst_gru_f32.hip", "inst_gru_bf16.hip", "inst_lstm_f32.hip",
-           "inst_lstm_bf16.hip", "inst_scan.hip", "inst_seq.hip"]
+           "inst_lstm_bf16.hip", "inst_scan.hip", "inst_seq.hip",
+           "inst_project.hip"]
 
 
 def _run(cmd, verbose):

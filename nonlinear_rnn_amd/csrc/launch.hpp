@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "adjoint.hpp"
+#include "project.hpp"
 #include "scan_kernel.hpp"
 #include "sequential.hpp"
 #include "solve.hpp"
@@ -35,6 +36,9 @@ PARARNN_DECLARE_LAUNCHERS(gru_bf16)
 PARARNN_DECLARE_LAUNCHERS(lstm_f32)
 PARARNN_DECLARE_LAUNCHERS(lstm_bf16)
 #undef PARARNN_DECLARE_LAUNCHERS
+
+// Input projection u = W x + b (MFMA).
+hipError_t launch_project(hipStream_t st, const ProjArgs &a);
 
 // Step-by-step application, one lane per channel.
 hipError_t launch_sequential(bool lstm, bool bf16, hipStream_t st, const SeqArgs &a);

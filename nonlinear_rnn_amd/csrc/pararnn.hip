@@ -364,6 +364,43 @@ pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
                                                                                   : PARARNN_ERR_HIP;
 }
 
+pararnn_status_t pararnn_project(const pararnn_proj_shape_t *sh, const void *x, const void *w,
+                                 const float *bias, void *u, pararnn_dtype_t u_dtype,
+                                 void *stream)
+{
+    if (!sh) return PARARNN_ERR_INVALID;
+    if (sh->B < 0 || sh->T < 0 || sh->I < 0 || sh->M < 0) return PARARNN_ERR_INVALID;
+    if (u_dtype != PARARNN_F32 && u_dtype != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;
+    if (sh->B == 0 || sh->T == 0 || sh->M == 0) return PARARNN_OK;
+    // rows must not overlap: x rows of I elements, W rows of I, u rows of T
+    if (sh->x_stride_t < sh->I || sh->x_stride_b < sh->x_stride_t * sh->T) return PARARNN_ERR_INVALID;
+    if (sh->w_stride_m < sh->I) return PARARNN_ERR_INVALID;
+    if (sh->u_stride_m < sh->T || sh->u_stride_b < sh->u_stride_m * sh->M) return PARARNN_ERR_INVALID;
+    if (!u || (sh->I > 0 && (!x || !w))) return PARARNN_ERR_INVALID;
+    ProjArgs A;
+    std::memset(&A, 0, sizeof(A));
+    A.x = static_cast<const uint16_t *>(x);
+    A.w = static_cast<const uint16_t *>(w);
+    A.bias = bias;
+    A.u = u;
+    A.B = sh->B;
+    A.T = sh->T;
+    A.I = sh->I;
+    A.M = sh->M;
+    A.xsb = sh->x_stride_b;
+    A.xst = sh->x_stride_t;
+    A.wsm = sh->w_stride_m;
+    A.usb = sh->u_stride_b;
+    A.usm = sh->u_stride_m;
+    A.out_bf16 = u_dtype == PARARNN_BF16 ? 1 : 0;
+    const int64_t tm = (sh->M + proj::kBM - 1) / proj::kBM, tn = (sh->T + proj::kBN - 1) / proj::kBN;
+    if (tm * tn * sh->B >= (int64_t(1) << 31)) return PARARNN_ERR_UNSUPPORTED;
+    A.tiles_m = (int32_t)tm;
+    A.tiles_n = (int32_t)tn;
+    const hipError_t e = launch_project(static_cast<hipStream_t>(stream), A);
+    return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+}
+
 pararnn_status_t pararnn_sequential(pararnn_cell_t cell, const pararnn_shape_t *shape,
                                     const void *const *u, pararnn_dtype_t u_dtype,
                                     const float *a, const float *const *s0, float *const *s,

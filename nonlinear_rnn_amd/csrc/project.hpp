@@ -1,0 +1,199 @@
+// Input projection u = W x + b, the dense step before the recurrence: every
+// gate's pre-activation input u_t = W x_t + b is computed once for the whole
+// sequence before the Newton solve (the cells of the voguetech.ru ParaRNN
+// article, "Что именно сделали технически", item 3, take u as precomputed
+// projections; only the diagonal recurrent part stays inside the solve).
+//
+// Per batch row b it is one matrix product
+//     u[b][m][t] = sum_k W[m][k] x[b][t][k] + bias[m],   m < M = G*D, t < T,
+// with W [M][I] and x [B][T][I] both contiguous along k: the MFMA operand
+// layout needs no transpose, and the output comes out channel-major with
+// time contiguous — the [B][G*D][T] layout the solve reads (gate g's plane
+// starts at row g*D).  bf16 operands, fp32 accumulation on the matrix cores
+// (v_mfma_f32_32x32x16_bf16), fp32 or bf16 (round to nearest even) output.
+//
+// Tiling: a 256-thread workgroup computes a 256 (m) x 128 (t) tile; each of
+// its 4 waves a 128 x 64 tile as 4 x 2 MFMA 32x32 blocks (128 accumulator
+// VGPRs).  K advances 32 at a time through two LDS stages: while the waves
+// multiply out of one stage, the next stage's operands are in flight from
+// HBM into registers and are written to the other stage afterwards (one
+// barrier per step).  LDS rows are padded to 80 bytes so the 16-byte operand
+// reads of 16 lanes cover all 64 banks once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pararnn {
+
+struct ProjArgs {
+    const uint16_t *x;   // bf16 bits, x[b][t][k] at b*xsb + t*xst + k
+    const uint16_t *w;   // bf16 bits, W[m][k] at m*wsm + k
+    const float *bias;   // [M] or null
+    void *u;             // u[b][m][t] at b*usb + m*usm + t
+    int64_t B, T, I, M;
+    int64_t xsb, xst, wsm, usb, usm;
+    int32_t out_bf16;
+    int32_t tiles_m, tiles_n;  // workgroup tiles along m and t
+};
+
+namespace proj {
+
+constexpr int kBM = 256, kBN = 128, kBK = 32;
+constexpr int kRow = kBK + 8;  // padded LDS row, bf16 elements (80 bytes)
+constexpr int kThreads = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
+{
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+// One 16-byte chunk (8 k-values) of a row, zero beyond the matrix.
+__device__ __forceinline__ uint4 load_chunk(const uint16_t *row, int64_t k, int64_t K,
+                                            bool row_ok, bool vec)
+{
+    if (!row_ok) return make_uint4(0u, 0u, 0u, 0u);
+    if (vec && k + 8 <= K) return *reinterpret_cast<const uint4 *>(row + k);
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (k + j < K) ? row[k + j] : (uint16_t)0;
+    uint4 v;
+    __builtin_memcpy(&v, e, 16);
+    return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace proj
+
+#ifdef PARARNN_DEFINE_PROJECT_KERNEL  // compiled once, in its own translation unit
+__global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
+{
+    using namespace proj;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM][kRow];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN][kRow];
+
+    // workgroup -> (batch row, m tile, t tile); m tiles vary fastest so the
+    // workgroups that share an x tile run together
+    int64_t g = blockIdx.x;
+    const int64_t tm = g % A.tiles_m;
+    g /= A.tiles_m;
+    const int64_t tn = g % A.tiles_n;
+    const int64_t b = g / A.tiles_n;
+    const int64_t m0 = tm * kBM, n0 = tn * kBN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*128, cols wn*64
+    const int64_t K = A.I;
+    const uint16_t *xb = A.x + b * A.xsb;
+    const bool wvec = (A.wsm % 8 == 0) && ((reinterpret_cast<uintptr_t>(A.w) & 15u) == 0);
+    const bool xvec = (A.xst % 8 == 0) && (A.xsb % 8 == 0) &&
+                      ((reinterpret_cast<uintptr_t>(A.x) & 15u) == 0);
+
+    // staging: A tile 256 rows x 4 chunks (4 per thread), B tile 128 x 4 (2)
+    uint4 ra[4], rb[2];
+    auto fetch = [&](int64_t k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = tid + j * kThreads;
+            const int64_t m = m0 + (c >> 2);
+            ra[j] = load_chunk(A.w + m * A.wsm, k0 + (c & 3) * 8, K, m < A.M, wvec);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = tid + j * kThreads;
+            const int64_t t = n0 + (c >> 2);
+            rb[j] = load_chunk(xb + t * A.xst, k0 + (c & 3) * 8, K, t < A.T, xvec);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = tid + j * kThreads;
+            *reinterpret_cast<uint4 *>(&As[buf][c >> 2][(c & 3) * 8]) = ra[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = tid + j * kThreads;
+            *reinterpret_cast<uint4 *>(&Bs[buf][c >> 2][(c & 3) * 8]) = rb[j];
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t steps = (K + kBK - 1) / kBK;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    const int ar = lane & 31, ak = (lane >> 5) * 8;  // operand row and k offset of this lane
+    for (int64_t s = 0; s < steps; ++s) {
+        const int buf = (int)(s & 1);
+        if (s + 1 < steps) fetch((s + 1) * kBK);
+#pragma unroll
+        for (int h = 0; h < kBK / 16; ++h) {
+            bf16x8 fa[4], fb[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fa[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                    &As[buf][wm * 128 + i * 32 + ar][h * 16 + ak]));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                fb[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                    &Bs[buf][wn * 64 + j * 32 + ar][h * 16 + ak]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
+                                                                        0, 0, 0);
+        }
+        if (s + 1 < steps) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: accumulator r of block (i, j) holds row
+    // 8 (r / 4) + 4 (lane / 32) + r % 4 and column lane % 32 of that block
+    const int64_t col_base = n0 + wn * 64 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m >= A.M) continue;
+            const float bias = A.bias ? A.bias[m] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t t = col_base + j * 32;
+                if (t >= A.T) continue;
+                const float v = acc[i][j][r] + bias;
+                const int64_t off = b * A.usb + m * A.usm + t;
+                if (A.out_bf16)
+                    static_cast<uint16_t *>(A.u)[off] = f32_to_bf16_rne(v);
+                else
+                    static_cast<float *>(A.u)[off] = v;
+            }
+        }
+    }
+}
+#endif
+
+}  // namespace pararnn

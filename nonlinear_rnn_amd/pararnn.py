@@ -37,6 +37,13 @@ class Shape(ctypes.Structure):
                 ("s_stride_b", ctypes.c_int64), ("s_stride_d", ctypes.c_int64)]
 
 
+class ProjShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("M", ctypes.c_int64), ("x_stride_b", ctypes.c_int64),
+                ("x_stride_t", ctypes.c_int64), ("w_stride_m", ctypes.c_int64),
+                ("u_stride_b", ctypes.c_int64), ("u_stride_m", ctypes.c_int64)]
+
+
 class Newton(ctypes.Structure):
     _fields_ = [("tol", ctypes.c_float), ("max_iters", ctypes.c_int32),
                 ("steps_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
@@ -71,6 +78,8 @@ def load():
     lib.pararnn_solve_lstm.restype = i32
     lib.pararnn_solve_lstm.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, P(Newton), vp,
                                        vp, sz, vp]
+    lib.pararnn_project.restype = i32
+    lib.pararnn_project.argtypes = [P(ProjShape), vp, vp, vp, vp, i32, vp]
     lib.pararnn_sequential.restype = i32
     lib.pararnn_sequential.argtypes = [i32, P(Shape), vp, i32, vp, vp, vp, vp]
     lib.pararnn_scan_workspace_bytes.restype = sz
@@ -299,6 +308,40 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
                                ctypes.byref(newton), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream_handle(stream)))
     return dict(du=du, da=da, ds0=ds0, lam=lam)
+
+
+def project(x, w, bias=None, *, out=None, out_dtype=torch.float32, stream=None):
+    """Input projection u[b][m][t] = sum_k w[m][k] x[b][t][k] + bias[m] on
+    the matrix cores.  x [B][T][I] and w [M][I] bfloat16 with the last (k)
+    dimension contiguous; bias float32 [M] or None.  Returns u [B][M][T]
+    (float32 or bfloat16); for M = G*D, u[:, g*D:(g+1)*D] is gate g's plane
+    for the solves."""
+    lib = load()
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("x and w must be bfloat16")
+    if x.dim() != 3 or w.dim() != 2 or x.shape[2] != w.shape[1]:
+        raise ValueError("x [B][T][I] and w [M][I] with matching I")
+    if (x.numel() and x.stride(2) != 1) or (w.numel() and w.stride(1) != 1):
+        raise ValueError("x and w must be contiguous along I")
+    B, T, I = x.shape
+    M = w.shape[0]
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (M,)
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [M]")
+    if out is None:
+        out = torch.empty((B, M, T), dtype=out_dtype, device=x.device)
+    if tuple(out.shape) != (B, M, T) or out.dtype not in (torch.float32, torch.bfloat16) or (
+            out.numel() and out.stride(2) != 1):
+        raise ValueError("out must be [B][M][T] float32 or bfloat16, time contiguous")
+    # strides of size-1 dimensions are arbitrary in torch: use dense ones
+    xst = x.stride(1) if T > 1 else I
+    usm = out.stride(1) if M > 1 else T
+    sh = ProjShape(B, T, I, M, x.stride(0) if B > 1 else xst * T, xst,
+                   w.stride(0) if M > 1 else I, out.stride(0) if B > 1 else usm * M, usm)
+    dt = BF16 if out.dtype == torch.bfloat16 else F32
+    _check(lib.pararnn_project(ctypes.byref(sh), _ptr(x), _ptr(w), _ptr(bias), _ptr(out), dt,
+                               _stream_handle(stream)))
+    return out
 
 
 def sequential(cell, u, a, s0, *, out=None, stream=None):

@@ -169,3 +169,24 @@ def test_sequential_rejects_bad_arguments_before_any_device_call():
     assert lib.pararnn_sequential(0, ctypes.byref(bad), u, 0, one, s, s, None) == 1
     empty = pr.make_shape(0, 16, 3)
     assert lib.pararnn_sequential(0, ctypes.byref(empty), None, 0, None, None, None, None) == 0
+
+
+def test_project_rejects_bad_arguments_before_any_device_call():
+    lib = pr.load()
+    one = ctypes.c_void_p(16)
+
+    def call(sh, dt=0, x=one, w=one, u=one):
+        return lib.pararnn_project(ctypes.byref(sh) if sh is not None else None, x, w, None, u,
+                                   dt, None)
+
+    good = pr.ProjShape(2, 8, 4, 6, 32, 4, 4, 48, 8)
+    assert call(None) == 1
+    assert call(pr.ProjShape(-1, 8, 4, 6, 32, 4, 4, 48, 8)) == 1
+    assert call(good, dt=7) == 2
+    assert call(pr.ProjShape(2, 8, 4, 6, 32, 3, 4, 48, 8)) == 1   # x rows overlap
+    assert call(pr.ProjShape(2, 8, 4, 6, 31, 4, 4, 48, 8)) == 1   # x batches overlap
+    assert call(pr.ProjShape(2, 8, 4, 6, 32, 4, 3, 48, 8)) == 1   # W rows overlap
+    assert call(pr.ProjShape(2, 8, 4, 6, 32, 4, 4, 47, 8)) == 1   # u batches overlap
+    assert call(good, x=None) == 1
+    assert call(good, u=None) == 1
+    assert call(pr.ProjShape(0, 8, 4, 6, 32, 4, 4, 48, 8), x=None, w=None, u=None) == 0

@@ -1,0 +1,102 @@
+"""GPU parity of the input projection (pararnn_project, MFMA) against the
+float64 oracle on the same bf16 operands.
+
+Bound: any order of summing the K exact products in float32 is within
+K * 2^-24 * sum_k |w x| of the exact sum (plus the bias add); bfloat16
+output adds one rounding, 2^-8 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nonlinear_rnn_amd import pararnn as pr
+from oracle import projection
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def bf16(a):
+    """float32 array -> (torch bfloat16 on device, float64 numpy of the same values)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+    return t.to(DEV), t.to(torch.float64).numpy()
+
+
+def check(got, x64, w64, bias, out_bf16=False):
+    ref = projection.project(x64, w64, bias)
+    scale = projection.project_abs(x64, w64, bias)
+    K = x64.shape[2]
+    bound = (K + 2) * 2.0 ** -24 * scale + 1e-30
+    if out_bf16:
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(got.to(torch.float64).cpu().numpy() - ref)
+    assert np.all(err <= bound), (float(err.max()), float((err / bound).max()))
+
+
+@pytest.mark.parametrize("B,T,I,M", [(2, 128, 64, 256), (1, 100, 40, 300), (3, 257, 1024, 288),
+                                     (2, 384, 96, 768), (1, 1, 8, 1), (2, 130, 33, 257)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_project_parity(B, T, I, M, out_dtype):
+    rng = np.random.default_rng(B * 1000 + T + I + M)
+    x, x64 = bf16(rng.standard_normal((B, T, I)))
+    w, w64 = bf16(rng.standard_normal((M, I)) / np.sqrt(I))
+    bias = rng.standard_normal(M).astype(np.float32)
+    u = pr.project(x, w, torch.from_numpy(bias).to(DEV), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    check(u, x64, w64, bias.astype(np.float64), out_bf16=out_dtype == torch.bfloat16)
+
+
+def test_project_no_bias_and_empty_inner_dimension():
+    rng = np.random.default_rng(5)
+    x, x64 = bf16(rng.standard_normal((2, 64, 48)))
+    w, w64 = bf16(rng.standard_normal((256, 48)))
+    u = pr.project(x, w)
+    torch.cuda.synchronize()
+    check(u, x64, w64, None)
+    bias = torch.arange(5, dtype=torch.float32, device=DEV)
+    u0 = pr.project(torch.empty((1, 3, 0), dtype=torch.bfloat16, device=DEV),
+                    torch.empty((5, 0), dtype=torch.bfloat16, device=DEV), bias)
+    torch.cuda.synchronize()
+    assert torch.equal(u0, bias[None, :, None].expand(1, 5, 3))
+
+
+def test_project_strided_views():
+    """x and w as views into wider rows (k stride 1, row strides not 8-multiples
+    or not 16-byte aligned), output as a view into a wider buffer."""
+    rng = np.random.default_rng(6)
+    xb, _ = bf16(rng.standard_normal((2, 70, 45)))
+    wb, _ = bf16(rng.standard_normal((300, 41)))
+    x = xb[:, 3:68, 1:41]
+    w = wb[:, 1:41]
+    x64 = x.to(torch.float64).cpu().numpy()
+    w64 = w.to(torch.float64).cpu().numpy()
+    big = torch.full((2, 310, 80), 7.0, device=DEV)
+    out = big[:, 5:305, 2:67]
+    pr.project(x, w, out=out)
+    torch.cuda.synchronize()
+    check(out, x64, w64, None)
+    assert float(big[:, :5].sub(7).abs().max()) == 0.0
+    assert float(big[:, :, :2].sub(7).abs().max()) == 0.0
+    assert float(big[:, :, 67:].sub(7).abs().max()) == 0.0
+
+
+def test_projection_feeds_the_solve():
+    """x -> u (bf16 planes of one [B][3D][T] buffer) -> ParaGRU solve, against
+    the oracle solve on the oracle projection rounded to bf16 the same way."""
+    from oracle import sequential as seq
+    B, T, I, D = 2, 512, 64, 32
+    rng = np.random.default_rng(7)
+    x, x64 = bf16(rng.standard_normal((B, T, I)))
+    w, w64 = bf16(rng.standard_normal((3 * D, I)) / np.sqrt(I))
+    u = pr.project(x, w, out_dtype=torch.bfloat16)
+    planes = [u[:, g * D:(g + 1) * D] for g in range(3)]
+    a = torch.from_numpy(rng.uniform(-1, 1, (3, D)).astype(np.float32)).to(DEV)
+    h0 = torch.zeros((B, D), device=DEV)
+    h, info = pr.solve_gru(planes, a, h0, tol=1e-6, max_iters=30)
+    assert pr.read_info(info)["converged"]
+    # oracle: the device's bf16 projections (checked above against the fp64
+    # product), solved sequentially in fp64
+    u_dev = [np.ascontiguousarray(p.to(torch.float32).cpu().numpy()) for p in planes]
+    ref = seq.gru_forward(u_dev, a.cpu().numpy(), h0.cpu().numpy())
+    assert np.max(np.abs(h.cpu().numpy() - ref)) < 1e-5
+    check(u, x64, w64, None, out_bf16=True)
