@@ -122,6 +122,63 @@ def cpu_baseline(w, inp, budget_s=12.0):
                       f"OpenMP over channels), mean of {reps} runs, {dt:.3f} s each"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def bench_project(w, args):
+    """The input projection for the workload: x [B][T][I = D] and W [G*D][I]
+    bf16 (seeded N(0,1), W scaled by 1/sqrt(I)), bias f32, output in the
+    workload's projection dtype.  One step = one projection of the batch."""
+    import numpy as np
+    import torch
+    from nonlinear_rnn_amd import pararnn as pr
+
+    dev = "cuda:0"
+    I, M = w.D, w.G * w.D
+    rng = np.random.default_rng(w.seed + 100)
+    gen = torch.Generator(device="cpu").manual_seed(w.seed + 100)
+    x = torch.randn((w.B, w.T, I), generator=gen).to(torch.bfloat16).to(dev)
+    wt = (torch.randn((M, I), generator=gen) / I ** 0.5).to(torch.bfloat16).to(dev)
+    bias = torch.from_numpy(rng.standard_normal(M).astype(np.float32)).to(dev)
+    out_dtype = torch.bfloat16 if w.u_dtype == "bf16" else torch.float32
+    out = torch.empty((w.B, M, w.T), dtype=out_dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pr.project(x, wt, bias, out=out, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        pr.project(x, wt, bias, out=out, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    kavg = sum(ms) / len(ms)
+    flops = 2.0 * w.B * w.T * I * M
+    tflops = flops / (kavg * 1e-3) / 1e12
+    ob = 2 if out_dtype == torch.bfloat16 else 4
+    nbytes = w.B * w.T * I * 2 + M * I * 2 + M * 4 + w.B * M * w.T * ob
+    return {
+        "metric": "input projection TFLOP/s (u = W x + b, bf16 in, fp32 accumulate)",
+        "value": flops / (wall / args.steps) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic (torch.randn seed {w.seed + 100}: x~N(0,1), W~N(0,1/I), bias~N(0,1))",
+        "config": {"workload": f"projection for {w.name}", "B": w.B, "T": w.T, "I": I, "M": M,
+                   "out_dtype": "bf16" if ob == 2 else "f32"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "algorithmic_bytes": nbytes, "kernel": "project_kernel",
+                     "kernel_ms_avg": kavg, "kernel_ms_min": min(ms),
+                     "hbm": {"achieved": nbytes / (kavg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s",
+                             "frac": nbytes / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS}},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +186,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gru_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["solve", "project"], default="solve",
+                    help="solve: the Newton solve (default); project: the input projection "
+                         "u = W x + b for the workload's shapes with I = D inputs")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB three "
                          "times (plain device copy used to calibrate HBM byte counters)")
@@ -147,6 +207,9 @@ def main():
     from nonlinear_rnn_amd.inputs import WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
+    if args.op == "project":
+        print(json.dumps(bench_project(w, args)), flush=True)
+        return
     inp = workload_inputs(w)
     dev = "cuda:0"
     if inp.u_bf16 is not None:

@@ -15,9 +15,10 @@
 // Tiling: a 256-thread workgroup computes a 256 (m) x 128 (t) tile; each of
 // its 4 waves a 128 x 64 tile as 4 x 2 MFMA 32x32 blocks (128 accumulator
 // VGPRs).  K advances 32 at a time through two LDS stages: while the waves
-// multiply out of one stage, the next stage's operands are in flight from
-// HBM into registers and are written to the other stage afterwards (one
-// barrier per step).  LDS rows are padded to 80 bytes so the 16-byte operand
+// multiply out of one stage, the next stage waits in registers to be written
+// to the other one and the stage after it is in flight from memory (one
+// barrier per step).  Tiles are ordered per XCD and in groups of m tiles so
+// that the workgroups in flight on one XCD share their operands in its L2.  LDS rows are padded to 80 bytes so the 16-byte operand
 // reads of 16 lanes cover all 64 banks once.
 #pragma once
 
@@ -36,6 +37,7 @@ struct ProjArgs {
     int64_t xsb, xst, wsm, usb, usm;
     int32_t out_bf16;
     int32_t tiles_m, tiles_n;  // workgroup tiles along m and t
+    int32_t group_m;           // m tiles that walk the t tiles together
 };
 
 namespace proj {
@@ -85,13 +87,23 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM][kRow];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN][kRow];
 
-    // workgroup -> (batch row, m tile, t tile); m tiles vary fastest so the
-    // workgroups that share an x tile run together
+    // Workgroup -> tile.  Workgroups are dealt to the 8 XCDs round-robin, so
+    // the hardware index is first turned into an index that runs
+    // contiguously within one XCD (whose L2 the tiles then share).  Within a
+    // batch row, groups of group_m m tiles walk the t tiles together: the
+    // workgroups in flight on an XCD share a few W tiles and each x tile.
+    const int64_t total = (int64_t)A.tiles_m * A.tiles_n * A.B;
     int64_t g = blockIdx.x;
-    const int64_t tm = g % A.tiles_m;
-    g /= A.tiles_m;
-    const int64_t tn = g % A.tiles_n;
-    const int64_t b = g / A.tiles_n;
+    if (total % 8 == 0) g = (g % 8) * (total / 8) + g / 8;
+    const int64_t per_b = (int64_t)A.tiles_m * A.tiles_n;
+    const int64_t b = g / per_b;
+    const int64_t r = g - b * per_b;
+    const int64_t mg = r / ((int64_t)A.group_m * A.tiles_n);
+    const int64_t gsz = (A.tiles_m - mg * A.group_m) < A.group_m ? (A.tiles_m - mg * A.group_m)
+                                                                  : A.group_m;
+    const int64_t rr = r - mg * A.group_m * A.tiles_n;
+    const int64_t tn = rr / gsz;
+    const int64_t tm = mg * A.group_m + (rr - tn * gsz);
     const int64_t m0 = tm * kBM, n0 = tn * kBN;
 
     const int tid = threadIdx.x;
@@ -103,32 +115,35 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
     const bool xvec = (A.xst % 8 == 0) && (A.xsb % 8 == 0) &&
                       ((reinterpret_cast<uintptr_t>(A.x) & 15u) == 0);
 
-    // staging: A tile 256 rows x 4 chunks (4 per thread), B tile 128 x 4 (2)
-    uint4 ra[4], rb[2];
-    auto fetch = [&](int64_t k0) {
+    // staging: A tile 256 rows x 4 chunks (4 per thread), B tile 128 x 4
+    // (2); two sets, so a stage's loads have two steps to arrive
+    struct Stage {
+        uint4 a[4], b[2];
+    };
+    auto fetch = [&](Stage &st, int64_t k0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = tid + j * kThreads;
             const int64_t m = m0 + (c >> 2);
-            ra[j] = load_chunk(A.w + m * A.wsm, k0 + (c & 3) * 8, K, m < A.M, wvec);
+            st.a[j] = load_chunk(A.w + m * A.wsm, k0 + (c & 3) * 8, K, m < A.M, wvec);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = tid + j * kThreads;
             const int64_t t = n0 + (c >> 2);
-            rb[j] = load_chunk(xb + t * A.xst, k0 + (c & 3) * 8, K, t < A.T, xvec);
+            st.b[j] = load_chunk(xb + t * A.xst, k0 + (c & 3) * 8, K, t < A.T, xvec);
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](const Stage &st, int buf) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = tid + j * kThreads;
-            *reinterpret_cast<uint4 *>(&As[buf][c >> 2][(c & 3) * 8]) = ra[j];
+            *reinterpret_cast<uint4 *>(&As[buf][c >> 2][(c & 3) * 8]) = st.a[j];
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = tid + j * kThreads;
-            *reinterpret_cast<uint4 *>(&Bs[buf][c >> 2][(c & 3) * 8]) = rb[j];
+            *reinterpret_cast<uint4 *>(&Bs[buf][c >> 2][(c & 3) * 8]) = st.b[j];
         }
     };
 
@@ -141,13 +156,8 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int64_t steps = (K + kBK - 1) / kBK;
-    fetch(0);
-    stash(0);
-    __syncthreads();
     const int ar = lane & 31, ak = (lane >> 5) * 8;  // operand row and k offset of this lane
-    for (int64_t s = 0; s < steps; ++s) {
-        const int buf = (int)(s & 1);
-        if (s + 1 < steps) fetch((s + 1) * kBK);
+    auto mma = [&](int buf) {
 #pragma unroll
         for (int h = 0; h < kBK / 16; ++h) {
             bf16x8 fa[4], fb[2];
@@ -166,7 +176,21 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
                                                                         0, 0, 0);
         }
-        if (s + 1 < steps) stash(buf ^ 1);
+    };
+    // step s multiplies LDS stage s % 2 while stage s + 1 waits in registers
+    // (cur) and stage s + 2 is being loaded (nxt)
+    Stage cur, nxt;
+    if (steps > 0) {
+        fetch(cur, 0);
+        stash(cur, 0);
+    }
+    if (steps > 1) fetch(cur, kBK);
+    __syncthreads();
+    for (int64_t s = 0; s < steps; ++s) {
+        if (s + 2 < steps) fetch(nxt, (s + 2) * kBK);
+        mma((int)(s & 1));
+        if (s + 1 < steps) stash(cur, (int)((s + 1) & 1));
+        cur = nxt;
         __syncthreads();
     }
 
