@@ -15,9 +15,9 @@
 // Tiling: a 256-thread workgroup computes a 256 (m) x 128 (t) tile; each of
 // its 4 waves a 128 x 64 tile as 4 x 2 MFMA 32x32 blocks (128 accumulator
 // VGPRs).  K advances 32 at a time through two LDS stages: while the waves
-// multiply out of one stage, the next stage waits in registers to be written
-// to the other one and the stage after it is in flight from memory (one
-// barrier per step).  Tiles are ordered per XCD and in groups of m tiles so
+// multiply out of one stage, the next stage is in flight from memory into
+// registers and is written to the other one afterwards (one barrier per
+// step).  Tiles are ordered per XCD and in groups of m tiles so
 // that the workgroups in flight on one XCD share their operands in its L2.  LDS rows are padded to 80 bytes so the 16-byte operand
 // reads of 16 lanes cover all 64 banks once.
 #pragma once
@@ -42,8 +42,12 @@ struct ProjArgs {
 
 namespace proj {
 
-constexpr int kBM = 256, kBN = 128, kBK = 32;
-constexpr int kRow = kBK + 8;  // padded LDS row, bf16 elements (80 bytes)
+#ifndef PARARNN_PROJ_BK
+#define PARARNN_PROJ_BK 32
+#endif
+constexpr int kBM = 256, kBN = 128, kBK = PARARNN_PROJ_BK;
+constexpr int kRow = kBK + 8;   // padded LDS row, bf16 elements
+constexpr int kCR = kBK / 8;    // 16-byte chunks per row
 constexpr int kThreads = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -81,6 +85,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 }  // namespace proj
 
 #ifdef PARARNN_DEFINE_PROJECT_KERNEL  // compiled once, in its own translation unit
+// VEC: every row of x and W is 16-byte aligned and I % 32 == 0, so every
+// chunk of every stage lies inside its row: unconditional vector loads (rows
+// past M or T read a valid row whose results are not stored).
+template <bool VEC>
 __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
 {
     using namespace proj;
@@ -115,37 +123,48 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
     const bool xvec = (A.xst % 8 == 0) && (A.xsb % 8 == 0) &&
                       ((reinterpret_cast<uintptr_t>(A.x) & 15u) == 0);
 
-    // staging: A tile 256 rows x 4 chunks (4 per thread), B tile 128 x 4
-    // (2); two sets, so a stage's loads have two steps to arrive
-    struct Stage {
-        uint4 a[4], b[2];
-    };
-    auto fetch = [&](Stage &st, int64_t k0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tid + j * kThreads;
-            const int64_t m = m0 + (c >> 2);
-            st.a[j] = load_chunk(A.w + m * A.wsm, k0 + (c & 3) * 8, K, m < A.M, wvec);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = tid + j * kThreads;
-            const int64_t t = n0 + (c >> 2);
-            st.b[j] = load_chunk(xb + t * A.xst, k0 + (c & 3) * 8, K, t < A.T, xvec);
-        }
-    };
-    auto stash = [&](const Stage &st, int buf) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = tid + j * kThreads;
-            *reinterpret_cast<uint4 *>(&As[buf][c >> 2][(c & 3) * 8]) = st.a[j];
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = tid + j * kThreads;
-            *reinterpret_cast<uint4 *>(&Bs[buf][c >> 2][(c & 3) * 8]) = st.b[j];
-        }
-    };
+    // staging registers: the A tile is 256 rows x kCR chunks, the B tile
+    // 128 x kCR, spread over the 256 threads
+    constexpr int kAC = kBM * kCR / kThreads, kBC = kBN * kCR / kThreads;
+    uint4 ra[kAC], rb[kBC];
+#define PARARNN_PROJ_FETCH(K0)                                                                  \
+    do {                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < kAC; ++j)                                         \
+        {                                                                                       \
+            const int c = tid + j * kThreads;                                                   \
+            const int64_t m = m0 + c / kCR, k = (K0) + (c % kCR) * 8;                           \
+            if constexpr (VEC) {                                                                \
+                ra[j] = *reinterpret_cast<const uint4 *>(A.w + (m < A.M ? m : A.M - 1) * A.wsm + \
+                                                         k);                                    \
+            } else {                                                                            \
+                ra[j] = load_chunk(A.w + m * A.wsm, k, K, m < A.M, wvec);                       \
+            }                                                                                   \
+        }                                                                                       \
+        _Pragma("unroll") for (int j = 0; j < kBC; ++j)                                         \
+        {                                                                                       \
+            const int c = tid + j * kThreads;                                                   \
+            const int64_t t = n0 + c / kCR, k = (K0) + (c % kCR) * 8;                           \
+            if constexpr (VEC) {                                                                \
+                rb[j] = *reinterpret_cast<const uint4 *>(xb + (t < A.T ? t : A.T - 1) * A.xst + \
+                                                         k);                                    \
+            } else {                                                                            \
+                rb[j] = load_chunk(xb + t * A.xst, k, K, t < A.T, xvec);                        \
+            }                                                                                   \
+        }                                                                                       \
+    } while (0)
+#define PARARNN_PROJ_STASH(BUF)                                                                 \
+    do {                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < kAC; ++j)                                         \
+        {                                                                                       \
+            const int c = tid + j * kThreads;                                                   \
+            *reinterpret_cast<uint4 *>(&As[BUF][c / kCR][(c % kCR) * 8]) = ra[j];               \
+        }                                                                                       \
+        _Pragma("unroll") for (int j = 0; j < kBC; ++j)                                         \
+        {                                                                                       \
+            const int c = tid + j * kThreads;                                                   \
+            *reinterpret_cast<uint4 *>(&Bs[BUF][c / kCR][(c % kCR) * 8]) = rb[j];               \
+        }                                                                                       \
+    } while (0)
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -177,22 +196,25 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
                                                                         0, 0, 0);
         }
     };
-    // step s multiplies LDS stage s % 2 while stage s + 1 waits in registers
-    // (cur) and stage s + 2 is being loaded (nxt)
-    Stage cur, nxt;
+    // step s multiplies LDS stage s % 2 while stage s + 1 is in flight into
+    // the staging registers; it is written to the other stage afterwards.
+    // In the VEC case the loads are unconditional (past the last stage they
+    // reread it), so the compiler can count them instead of waiting for all.
+    const int64_t last = steps > 0 ? (steps - 1) * kBK : 0;
     if (steps > 0) {
-        fetch(cur, 0);
-        stash(cur, 0);
+        PARARNN_PROJ_FETCH(0);
+        PARARNN_PROJ_STASH(0);
     }
-    if (steps > 1) fetch(cur, kBK);
     __syncthreads();
     for (int64_t s = 0; s < steps; ++s) {
-        if (s + 2 < steps) fetch(nxt, (s + 2) * kBK);
+        const int64_t kn = (s + 1) * kBK < last ? (s + 1) * kBK : last;
+        if (VEC || s + 1 < steps) PARARNN_PROJ_FETCH(kn);
         mma((int)(s & 1));
-        if (s + 1 < steps) stash(cur, (int)((s + 1) & 1));
-        cur = nxt;
+        if (s + 1 < steps) PARARNN_PROJ_STASH((int)((s + 1) & 1));
         __syncthreads();
     }
+#undef PARARNN_PROJ_FETCH
+#undef PARARNN_PROJ_STASH
 
     // epilogue: accumulator r of block (i, j) holds row
     // 8 (r / 4) + 4 (lane / 32) + r % 4 and column lane % 32 of that block
