@@ -161,7 +161,16 @@ def bench_project(w, args):
     tflops = flops / (kavg * 1e-3) / 1e12
     ob = 2 if out_dtype == torch.bfloat16 else 4
     nbytes = w.B * w.T * I * 2 + M * I * 2 + M * 4 + w.B * M * w.T * ob
-    return {
+    extra = {}
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = n * 4
+    return dict({
         "metric": "input projection TFLOP/s (u = W x + b, bf16 in, fp32 accumulate)",
         "value": flops / (wall / args.steps) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
@@ -171,12 +180,13 @@ def bench_project(w, args):
                    "out_dtype": "bf16" if ob == 2 else "f32"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "algorithmic_bytes": nbytes, "kernel": "project_kernel",
+                     "traffic": measured_traffic("project_" + args.workload),
+                     "algorithmic_bytes": nbytes, "kernel": "project_kernel",
                      "kernel_ms_avg": kavg, "kernel_ms_min": min(ms),
                      "hbm": {"achieved": nbytes / (kavg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s",
                              "frac": nbytes / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS}},
-    }
+    }, **extra)
 
 
 def main():
