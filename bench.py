@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--op", choices=["solve", "project"], default="solve",
                     help="solve: the Newton solve (default); project: the input projection "
                          "u = W x + b for the workload's shapes with I = D inputs")
+    ap.add_argument("--layout", choices=["channel", "time"], default="channel",
+                    help="channel: [B][D][T] planes (default); time: the gate blocks of one "
+                         "[B][T][G*D] projection tensor and [B][T][D] states")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB three "
                          "times (plain device copy used to calibrate HBM byte counters)")
@@ -230,6 +233,17 @@ def main():
     a = torch.from_numpy(inp.a).to(dev)
     s0 = [torch.from_numpy(p).to(dev) for p in inp.s0]
     out = [torch.empty((w.B, w.D, w.T), dtype=torch.float32, device=dev) for _ in range(w.S)]
+    time_major = args.layout == "time"
+    if time_major:
+        # one [B][T][G*D] tensor (what a Linear over [B][T][I] inputs gives),
+        # passed per gate as strided views; states [B][T][D]
+        G, D = w.G, w.D
+        full = torch.empty((w.B, w.T, G * D), dtype=u[0].dtype, device=dev)
+        for g, p in enumerate(u):
+            full[:, :, g * D:(g + 1) * D] = p.transpose(1, 2)
+        u = [full[:, :, g * D:(g + 1) * D].transpose(1, 2) for g in range(G)]
+        out = [torch.empty((w.B, w.T, D), dtype=torch.float32, device=dev).transpose(1, 2)
+               for _ in range(w.S)]
     stream = torch.cuda.current_stream()
 
     def solve(info):
@@ -242,6 +256,14 @@ def main():
     adj_out = None
     if w.adjoint:
         gh = torch.from_numpy(inp.dh).to(dev)
+        if time_major:
+            gh = gh.transpose(1, 2).contiguous().transpose(1, 2)
+            du_full = torch.empty((w.B, w.T, w.G * w.D), dtype=torch.float32, device=dev)
+            adj_out = dict(du=[du_full[:, :, g * w.D:(g + 1) * w.D].transpose(1, 2)
+                               for g in range(w.G)],
+                           da=torch.empty((w.G, w.D), dtype=torch.float32, device=dev),
+                           ds0=[torch.empty((w.B, w.D), dtype=torch.float32, device=dev)
+                                for _ in range(w.S)], lam=None)
         gs = [None, gh] if w.cell == "lstm" else [gh]
 
     def backward():
@@ -299,7 +321,7 @@ def main():
     # the binding roof is the one the kernel runs closest to
     bound = "alu" if valu is not None and valu["frac"] > hbm["frac"] else "hbm"
     roof = valu if bound == "alu" else hbm
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload + ("_time_major" if time_major else ""))
     K, W, nb = pr.plan(w.cell, pr.make_shape(w.B, w.T, w.D))
     line = {
         "metric": METRIC,
@@ -315,6 +337,9 @@ def main():
         "dtype": "bf16-in/f32" if w.u_dtype == "bf16" else "f32",
         "data": data_recipe(w),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol,
+                   "layout": ("time-major: u gate blocks of one [B][T][G*D] tensor, "
+                              "states [B][T][D]") if time_major else
+                             "channel-major [B][D][T] planes",
                    "max_iters": w.max_iters, "seed": w.seed, "tiling": {"K": K, "W": W,
                    "time_blocks": nb}, "newton_updates": info["iters"],
                    "newton_updates_mean": info["iters_mean"], "converged": info["converged"],

@@ -30,10 +30,18 @@
  *     caller; the library never allocates, frees or synchronises.  All work
  *     is enqueued on `stream` (a hipStream_t, NULL = default stream) and the
  *     call returns before it completes.  Outputs must not alias inputs.
- *   - Layout: per-time-step planes are [B][D][T] with time contiguous
- *     (stride 1); element offset of (b, d, t) = b*stride_b + d*stride_d + t.
- *     Planes of `u` (and of `du`) use u_stride_*; state, gradient and lambda
- *     planes use s_stride_*.  Initial states are dense [B][D]; diagonal
+ *   - Layout: per-time-step planes are indexed (b, d, t); element offset of
+ *     (b, d, t) = b*stride_b + d*stride_d + t*stride_t.  Planes of `u` (and
+ *     of `du`) use u_stride_*; state, gradient and lambda planes use
+ *     s_stride_*.  The fast layout is channel-major [B][D][T] (stride_t = 1):
+ *     a lane's steps are contiguous and load as 16-byte vectors.  Any other
+ *     layout whose elements do not overlap is accepted, e.g. time-major
+ *     [B][T][D] (stride_t = D, stride_d = 1, as a [B][T][G*D] projection
+ *     gives per gate with stride_t = G*D): each step is then gathered with
+ *     its own 4-byte load (one L2 request per element; workgroups of
+ *     neighbouring channels run on one XCD, so HBM still sees each line about
+ *     once).  Measured 2-4x slower than channel-major for the Newton solve;
+ *     pararnn_project writes channel-major planes directly.  Initial states are dense [B][D]; diagonal
  *     weights are dense [G][D] float32 in gate order (GRU: z, r, c;
  *     LSTM: i, f, g, o).  LSTM state order is (c, h).
  *   - Errors: arguments are checked on the host before any HIP call; a bad
@@ -68,6 +76,7 @@ typedef struct {
     int64_t B, T, D;                 /* batch rows, time steps, channels     */
     int64_t u_stride_b, u_stride_d;  /* elements, every u / du plane         */
     int64_t s_stride_b, s_stride_d;  /* elements, every state/grad plane     */
+    int64_t u_stride_t, s_stride_t;  /* elements between steps (1: [B][D][T]) */
 } pararnn_shape_t;
 
 typedef struct {

@@ -32,6 +32,7 @@ struct AdjArgs {
     float *lam[2];
     int64_t B, T, D;
     int64_t usb, usd, ssb, ssd;
+    int64_t ust, sst;  // time strides (1 = channel-major)
     int64_t channels;
     int32_t nb;
     int32_t u_vec, du_vec, s_vec;
@@ -187,7 +188,7 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
         ticket_to_unit(s_ticket, A.nb, ch, q);
         k = A.nb - 1 - q;  // later time blocks take earlier tickets
     } else {
-        ch = blockIdx.x;
+        ch = xcd_channel(blockIdx.x, A.channels);
         k = 0;
     }
     if (ch >= A.channels) return;
@@ -209,7 +210,7 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float tmp[K];
-            load_steps<K, BF16>(A.u[g], uoff, t0, T, A.u_vec != 0, tmp);
+            load_steps<K, BF16>(A.u[g], uoff, t0, T, A.ust, A.u_vec != 0, tmp);
             const float sc = Cell::uscale(g);
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) u[kk][g] = tmp[kk] * sc;
@@ -218,17 +219,17 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
 #pragma unroll
         for (int c = 0; c < S; ++c) {
             float tmp[K];
-            load_steps<K, false>(A.s[c], soff, t0, T, A.s_vec != 0, tmp);
+            load_steps<K, false>(A.s[c], soff, t0, T, A.sst, A.s_vec != 0, tmp);
             float first = 0.0f;
             if (t0 == 0)
                 first = A.s0[c][b * A.D + d];
             else if (t0 - 1 < T)
-                first = A.s[c][soff + t0 - 1];
+                first = A.s[c][soff + (t0 - 1) * A.sst];
             vset(sp[0], c, first);
 #pragma unroll
             for (int kk = 1; kk < K; ++kk) vset(sp[kk], c, tmp[kk - 1]);
             if (A.gs[c]) {
-                load_steps<K, false>(A.gs[c], soff, t0, T, A.s_vec != 0, tmp);
+                load_steps<K, false>(A.gs[c], soff, t0, T, A.sst, A.s_vec != 0, tmp);
             } else {
 #pragma unroll
                 for (int kk = 0; kk < K; ++kk) tmp[kk] = 0.0f;
@@ -310,10 +311,10 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
         for (int c = 0; c < S; ++c) lo[c][kk] = vget(lam, c);
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) store_steps<K>(A.du[g] + uoff, t0, T, A.du_vec != 0, dpo[g]);
+    for (int g = 0; g < G; ++g) store_steps<K>(A.du[g] + uoff, t0, T, A.ust, A.du_vec != 0, dpo[g]);
     if (A.lam[0]) {
 #pragma unroll
-        for (int c = 0; c < S; ++c) store_steps<K>(A.lam[c] + soff, t0, T, A.s_vec != 0, lo[c]);
+        for (int c = 0; c < S; ++c) store_steps<K>(A.lam[c] + soff, t0, T, A.sst, A.s_vec != 0, lo[c]);
     }
     if (t0 == 0) {
 #pragma unroll

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 
 #define PARARNN_DEFINE_AUX_KERNELS
 #include "launch.hpp"
@@ -34,16 +35,29 @@ int cell_S(pararnn_cell_t c) { return c == PARARNN_LSTM ? 2 : 1; }
 int cell_G(pararnn_cell_t c) { return c == PARARNN_LSTM ? 4 : 3; }
 int rec_floats(pararnn_cell_t c) { return c == PARARNN_LSTM ? MapRec<Map2>::kFloats : MapRec<Map1>::kFloats; }
 
-// Rows (b, d) of a [B][D][T]-style plane must not overlap: either d-major
-// inside b (stride_d >= T, stride_b >= D stride_d) or b-major inside d.
-bool rows_disjoint(int64_t B, int64_t T, int64_t D, int64_t sb, int64_t sd)
+// Elements (b, d, t) of a plane must not overlap: with the dimensions of
+// extent > 1 taken in increasing stride, each stride must exceed the largest
+// offset the smaller ones reach.  Covers channel-major [B][D][T], time-major
+// [B][T][D] and any padded or permuted variant of them.
+bool planes_disjoint(int64_t B, int64_t T, int64_t D, int64_t sb, int64_t sd, int64_t st)
 {
-    if (sb < 0 || sd < 0) return false;
+    if (sb < 0 || sd < 0 || st < 0) return false;
     if (B == 0 || D == 0 || T == 0) return true;  // no elements
-    if (B <= 1 && D <= 1) return true;
-    if (B <= 1) return sd >= T;
-    if (D <= 1) return sb >= T;
-    return (sd >= T && sb >= D * sd) || (sb >= T && sd >= B * sb);
+    int64_t n[3] = {B, D, T}, str[3] = {sb, sd, st};
+    for (int i = 0; i < 3; ++i)  // sort by stride
+        for (int j = i + 1; j < 3; ++j)
+            if (str[j] < str[i]) {
+                std::swap(str[i], str[j]);
+                std::swap(n[i], n[j]);
+            }
+    __int128 reach = 0;  // largest offset of the smaller dimensions
+    for (int i = 0; i < 3; ++i) {
+        if (n[i] <= 1) continue;
+        if ((__int128)str[i] <= reach) return false;
+        reach += (__int128)str[i] * (n[i] - 1);
+        if (reach > (__int128)INT64_MAX) return false;
+    }
+    return true;
 }
 
 pararnn_status_t check_shape(const pararnn_shape_t *sh)
@@ -52,8 +66,10 @@ pararnn_status_t check_shape(const pararnn_shape_t *sh)
     if (sh->B < 0 || sh->T < 0 || sh->D < 0) return PARARNN_ERR_INVALID;
     if (sh->B > (int64_t(1) << 31) || sh->D > (int64_t(1) << 31) || sh->T > (int64_t(1) << 40))
         return PARARNN_ERR_UNSUPPORTED;
-    if (!rows_disjoint(sh->B, sh->T, sh->D, sh->u_stride_b, sh->u_stride_d)) return PARARNN_ERR_INVALID;
-    if (!rows_disjoint(sh->B, sh->T, sh->D, sh->s_stride_b, sh->s_stride_d)) return PARARNN_ERR_INVALID;
+    if (!planes_disjoint(sh->B, sh->T, sh->D, sh->u_stride_b, sh->u_stride_d, sh->u_stride_t))
+        return PARARNN_ERR_INVALID;
+    if (!planes_disjoint(sh->B, sh->T, sh->D, sh->s_stride_b, sh->s_stride_d, sh->s_stride_t))
+        return PARARNN_ERR_INVALID;
     return PARARNN_OK;
 }
 
@@ -115,7 +131,7 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
     pl.channels = sh->B * sh->D;
     pl.units = pl.channels * pl.nb;
     // dispatch packets count work-items in 32 bits
-    const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+    const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
     if (groups * kWave * W >= (int64_t(1) << 32)) return PARARNN_ERR_UNSUPPORTED;
     if (pl.nb >= kStopBase) return PARARNN_ERR_UNSUPPORTED;
     return PARARNN_OK;
@@ -196,6 +212,8 @@ pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, co
     A.usd = sh->u_stride_d;
     A.ssb = sh->s_stride_b;
     A.ssd = sh->s_stride_d;
+    A.ust = sh->u_stride_t;
+    A.sst = sh->s_stride_t;
     A.channels = pl.channels;
     A.tol = opt->tol;
     A.guess_tol = std::sqrt(opt->tol);
@@ -204,9 +222,11 @@ pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, co
     A.init_from_output = opt->init_from_output;
     A.info = info;
     const int ve = dt == PARARNN_BF16 ? 8 : 4;
-    bool uv = (sh->T % ve == 0) && (sh->u_stride_b % ve == 0) && (sh->u_stride_d % ve == 0);
+    bool uv = sh->u_stride_t == 1 && (sh->T % ve == 0) && (sh->u_stride_b % ve == 0) &&
+              (sh->u_stride_d % ve == 0);
     for (int g = 0; g < G && work; ++g) uv = uv && aligned16(u[g]);
-    bool sv = (sh->T % 4 == 0) && (sh->s_stride_b % 4 == 0) && (sh->s_stride_d % 4 == 0);
+    bool sv = sh->s_stride_t == 1 && (sh->T % 4 == 0) && (sh->s_stride_b % 4 == 0) &&
+              (sh->s_stride_d % 4 == 0);
     for (int c = 0; c < S && work; ++c) sv = sv && aligned16(s[c]);
     A.u_vec = uv ? 1 : 0;
     A.s_vec = sv ? 1 : 0;
@@ -228,7 +248,7 @@ pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, co
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
     }
     if (!work) return PARARNN_OK;
-    const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+    const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
     const int variant = sh->T % pl.P != 0 ? kNewtonAny
                         : pl.nb == 1      ? kNewtonFullSingle
                                           : kNewtonFull;
@@ -340,12 +360,16 @@ pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
     A.isd = shape->u_stride_d;
     A.osb = shape->s_stride_b;
     A.osd = shape->s_stride_d;
+    A.ist = shape->u_stride_t;
+    A.ost = shape->s_stride_t;
     A.channels = pl.channels;
     A.nb = (int32_t)pl.nb;
-    bool iv = (shape->T % 4 == 0) && (shape->u_stride_b % 4 == 0) && (shape->u_stride_d % 4 == 0);
+    bool iv = shape->u_stride_t == 1 && (shape->T % 4 == 0) && (shape->u_stride_b % 4 == 0) &&
+              (shape->u_stride_d % 4 == 0);
     for (int i = 0; i < S * S; ++i) iv = iv && aligned16(Am[i]);
     for (int c = 0; c < S; ++c) iv = iv && aligned16(bv[c]);
-    bool ov = (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) && (shape->s_stride_d % 4 == 0);
+    bool ov = shape->s_stride_t == 1 && (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) &&
+              (shape->s_stride_d % 4 == 0);
     for (int c = 0; c < S; ++c) ov = ov && aligned16(x[c]);
     A.in_vec = iv ? 1 : 0;
     A.out_vec = ov ? 1 : 0;
@@ -359,7 +383,7 @@ pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
                            0, strm, A, pl.units);
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
     }
-    const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+    const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
     return launch_scan(S, pl.K, pl.W, reverse != 0, groups, strm, A) == hipSuccess ? PARARNN_OK
                                                                                   : PARARNN_ERR_HIP;
 }
@@ -437,12 +461,15 @@ pararnn_status_t pararnn_sequential(pararnn_cell_t cell, const pararnn_shape_t *
     A.usd = shape->u_stride_d;
     A.ssb = shape->s_stride_b;
     A.ssd = shape->s_stride_d;
+    A.ust = shape->u_stride_t;
+    A.sst = shape->s_stride_t;
     A.channels = channels;
     const int ve = u_dtype == PARARNN_BF16 ? 8 : 4;
-    bool uv = (shape->T % ve == 0) && (shape->u_stride_b % ve == 0) &&
+    bool uv = shape->u_stride_t == 1 && (shape->T % ve == 0) && (shape->u_stride_b % ve == 0) &&
               (shape->u_stride_d % ve == 0);
     for (int g = 0; g < G; ++g) uv = uv && aligned16(u[g]);
-    bool sv = (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) && (shape->s_stride_d % 4 == 0);
+    bool sv = shape->s_stride_t == 1 && (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) &&
+              (shape->s_stride_d % 4 == 0);
     for (int c = 0; c < S; ++c) sv = sv && aligned16(s[c]);
     A.u_vec = uv ? 1 : 0;
     A.s_vec = sv ? 1 : 0;
@@ -557,16 +584,21 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
     A.usd = shape->u_stride_d;
     A.ssb = shape->s_stride_b;
     A.ssd = shape->s_stride_d;
+    A.ust = shape->u_stride_t;
+    A.sst = shape->s_stride_t;
     A.channels = pl.channels;
     A.nb = (int32_t)pl.nb;
     const int ve = u_dtype == PARARNN_BF16 ? 8 : 4;
-    bool uv = (shape->T % ve == 0) && (shape->u_stride_b % ve == 0) && (shape->u_stride_d % ve == 0);
-    bool dv = (shape->T % 4 == 0) && (shape->u_stride_b % 4 == 0) && (shape->u_stride_d % 4 == 0);
+    bool uv = shape->u_stride_t == 1 && (shape->T % ve == 0) && (shape->u_stride_b % ve == 0) &&
+              (shape->u_stride_d % ve == 0);
+    bool dv = shape->u_stride_t == 1 && (shape->T % 4 == 0) && (shape->u_stride_b % 4 == 0) &&
+              (shape->u_stride_d % 4 == 0);
     for (int g = 0; g < G && work; ++g) {
         uv = uv && aligned16(u[g]);
         dv = dv && aligned16(du[g]);
     }
-    bool sv = (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) && (shape->s_stride_d % 4 == 0);
+    bool sv = shape->s_stride_t == 1 && (shape->T % 4 == 0) && (shape->s_stride_b % 4 == 0) &&
+              (shape->s_stride_d % 4 == 0);
     for (int c = 0; c < S && work; ++c) {
         sv = sv && aligned16(s[c]);
         if (gs[c]) sv = sv && aligned16(gs[c]);
@@ -593,7 +625,7 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
     }
     if (work) {
-        const int64_t groups = pl.nb > 1 ? ((pl.channels + 7) / 8) * 8 * pl.nb : pl.channels;
+        const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
         hipError_t e;
         if (cell == PARARNN_GRU)
             e = u_dtype == PARARNN_BF16 ? launch_adjoint_gru_bf16(pl.K, pl.W, groups, strm, A)

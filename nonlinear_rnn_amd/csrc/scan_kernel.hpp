@@ -25,6 +25,7 @@ struct ScanArgs {
     float *x[2];         // S planes out
     int64_t B, T, D;
     int64_t isb, isd, osb, osd;
+    int64_t ist, ost;  // time strides (1 = channel-major)
     int64_t channels;
     int32_t nb;
     int32_t in_vec, out_vec;
@@ -44,8 +45,8 @@ struct ScanIo<Map1> {
                                                 Map1 (&m)[K])
     {
         float a[K], b[K];
-        load_steps<K, false>(A.A[0], off, t0, A.T, A.in_vec != 0, a);
-        load_steps<K, false>(A.b[0], off, t0, A.T, A.in_vec != 0, b);
+        load_steps<K, false>(A.A[0], off, t0, A.T, A.ist, A.in_vec != 0, a);
+        load_steps<K, false>(A.b[0], off, t0, A.T, A.ist, A.in_vec != 0, b);
 #pragma unroll
         for (int k = 0; k < K; ++k) m[k] = {a[k], b[k]};
     }
@@ -60,12 +61,12 @@ struct ScanIo<Map2> {
     {
         float a00[K], a01[K], a10[K], a11[K], b0[K], b1[K];
         const bool v = A.in_vec != 0;
-        load_steps<K, false>(A.A[0], off, t0, A.T, v, a00);
-        load_steps<K, false>(A.A[1], off, t0, A.T, v, a01);
-        load_steps<K, false>(A.A[2], off, t0, A.T, v, a10);
-        load_steps<K, false>(A.A[3], off, t0, A.T, v, a11);
-        load_steps<K, false>(A.b[0], off, t0, A.T, v, b0);
-        load_steps<K, false>(A.b[1], off, t0, A.T, v, b1);
+        load_steps<K, false>(A.A[0], off, t0, A.T, A.ist, v, a00);
+        load_steps<K, false>(A.A[1], off, t0, A.T, A.ist, v, a01);
+        load_steps<K, false>(A.A[2], off, t0, A.T, A.ist, v, a10);
+        load_steps<K, false>(A.A[3], off, t0, A.T, A.ist, v, a11);
+        load_steps<K, false>(A.b[0], off, t0, A.T, A.ist, v, b0);
+        load_steps<K, false>(A.b[1], off, t0, A.T, A.ist, v, b1);
 #pragma unroll
         for (int k = 0; k < K; ++k) m[k] = {a00[k], a01[k], a10[k], a11[k], b0[k], b1[k]};
     }
@@ -92,7 +93,7 @@ __global__ void __launch_bounds__(W * kWave) scan_kernel(ScanArgs A)
         __syncthreads();
         ticket_to_unit(s_ticket, A.nb, ch, r);
     } else {
-        ch = blockIdx.x;
+        ch = xcd_channel(blockIdx.x, A.channels);
         r = 0;
     }
     if (ch >= A.channels) return;
@@ -168,7 +169,7 @@ __global__ void __launch_bounds__(W * kWave) scan_kernel(ScanArgs A)
         for (int c = 0; c < S; ++c) xo[c][kk] = vget(xv, c);
     }
 #pragma unroll
-    for (int c = 0; c < S; ++c) store_steps<K>(A.x[c] + ooff, t0, T, A.out_vec != 0, xo[c]);
+    for (int c = 0; c < S; ++c) store_steps<K>(A.x[c] + ooff, t0, T, A.ost, A.out_vec != 0, xo[c]);
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS

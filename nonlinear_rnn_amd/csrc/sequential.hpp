@@ -26,6 +26,7 @@ struct SeqArgs {
     float *s[2];
     int64_t T, D;
     int64_t usb, usd, ssb, ssd;
+    int64_t ust, sst;  // time strides (1 = channel-major)
     int64_t channels;
     int32_t u_vec, s_vec;
 };
@@ -36,7 +37,7 @@ __device__ __forceinline__ void seq_load_chunk(const SeqArgs &A, int64_t uoff, i
 {
 #pragma unroll
     for (int g = 0; g < Cell::G; ++g) {
-        load_steps<K, BF16>(A.u[g], uoff, t0, A.T, A.u_vec != 0, u[g]);
+        load_steps<K, BF16>(A.u[g], uoff, t0, A.T, A.ust, A.u_vec != 0, u[g]);
         const float sc = Cell::uscale(g);
 #pragma unroll
         for (int k = 0; k < K; ++k) u[g][k] *= sc;
@@ -72,7 +73,7 @@ __global__ void __launch_bounds__(kWave) sequential_kernel(SeqArgs A)
             for (int c = 0; c < S; ++c) out[c][k] = vget(st, c);
         }
 #pragma unroll
-        for (int c = 0; c < S; ++c) store_steps<K>(A.s[c] + soff, t0, A.T, A.s_vec != 0, out[c]);
+        for (int c = 0; c < S; ++c) store_steps<K>(A.s[c] + soff, t0, A.T, A.sst, A.s_vec != 0, out[c]);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll

@@ -57,6 +57,7 @@ struct SolveArgs {
     float *s[2];
     int64_t B, T, D;
     int64_t usb, usd, ssb, ssd;
+    int64_t ust, sst;  // time strides (1 = channel-major)
     int64_t channels;
     float tol;
     float guess_tol;  // max|r| below which the next evaluation is guessed to be the last (0 = never)
@@ -113,12 +114,13 @@ __device__ __forceinline__ uint32_t rec_cbit(const float *r, int n)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// K consecutive steps t0..t0+K-1 of one plane, zero beyond T.  `vec` (uniform)
-// means T, the row strides and the base are multiples of 16 bytes, so 16-byte
-// vectors never straddle T.
+// K consecutive steps t0..t0+K-1 of one plane (steps `st` elements apart),
+// zero beyond T.  `vec` (uniform) means st = 1 and T, the row strides and the
+// base are multiples of 16 bytes, so 16-byte vectors never straddle T;
+// otherwise every step is its own load.
 template <int K, bool BF16>
 __device__ __forceinline__ void load_steps(const void *base, int64_t off, int64_t t0, int64_t T,
-                                           bool vec, float (&out)[K])
+                                           int64_t st, bool vec, float (&out)[K])
 {
     if constexpr (BF16) {
         const uint16_t *p = static_cast<const uint16_t *>(base) + off;
@@ -138,8 +140,9 @@ __device__ __forceinline__ void load_steps(const void *base, int64_t off, int64_
                 return;
             }
         }
+        const uint16_t *q = p + t0 * st;
 #pragma unroll
-        for (int k = 0; k < K; ++k) out[k] = (t0 + k < T) ? bf16_to_f32(p[t0 + k]) : 0.0f;
+        for (int k = 0; k < K; ++k) out[k] = (t0 + k < T) ? bf16_to_f32(q[k * st]) : 0.0f;
     } else {
         const float *p = static_cast<const float *>(base) + off;
         if constexpr (K % 4 == 0) {
@@ -156,13 +159,14 @@ __device__ __forceinline__ void load_steps(const void *base, int64_t off, int64_
                 return;
             }
         }
+        const float *q = p + t0 * st;
 #pragma unroll
-        for (int k = 0; k < K; ++k) out[k] = (t0 + k < T) ? p[t0 + k] : 0.0f;
+        for (int k = 0; k < K; ++k) out[k] = (t0 + k < T) ? q[k * st] : 0.0f;
     }
 }
 
 template <int K>
-__device__ __forceinline__ void store_steps(float *p, int64_t t0, int64_t T, bool vec,
+__device__ __forceinline__ void store_steps(float *p, int64_t t0, int64_t T, int64_t st, bool vec,
                                             const float (&v)[K])
 {
     if constexpr (K % 4 == 0) {
@@ -175,9 +179,21 @@ __device__ __forceinline__ void store_steps(float *p, int64_t t0, int64_t T, boo
             return;
         }
     }
+    float *q = p + t0 * st;
 #pragma unroll
     for (int k = 0; k < K; ++k)
-        if (t0 + k < T) p[t0 + k] = v[k];
+        if (t0 + k < T) q[k * st] = v[k];
+}
+
+// Channel of workgroup `blk` when every channel is one work unit and the
+// grid is 8 * ceil(n / 8): workgroups are dispatched round-robin over the 8
+// XCDs, and each XCD gets a contiguous range of channels, so channels that
+// share cache lines (time-major planes) share an L2 and run close in time.
+// Returns a value >= n for the padding workgroups.
+__device__ __forceinline__ int64_t xcd_channel(int64_t blk, int64_t n)
+{
+    const int64_t per = (n + 7) >> 3;
+    return (blk & 7) * per + (blk >> 3);
 }
 
 template <class V>
@@ -324,7 +340,7 @@ __device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uof
 #pragma unroll
     for (int g = 0; g < Cell::G; ++g) {
         float tmp[K];
-        load_steps<K, BF16>(A.u[g], uoff, t0, A.T, A.u_vec != 0, tmp);
+        load_steps<K, BF16>(A.u[g], uoff, t0, A.T, A.ust, A.u_vec != 0, tmp);
         const float sc = Cell::uscale(g);
 #pragma unroll
         for (int kk = 0; kk < K; ++kk) u[kk][g] = tmp[kk] * sc;
@@ -476,7 +492,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         float tmp[K];
 #pragma unroll
         for (int kk = 0; kk < K; ++kk) tmp[kk] = vget(s[kk], c);
-        store_steps<K>(A.s[c] + soff, t0, T, A.s_vec != 0, tmp);
+        store_steps<K>(A.s[c] + soff, t0, T, A.sst, A.s_vec != 0, tmp);
     }
     if (A.info && threadIdx.x == 0) {
         pararnn_info_t *inf = A.info;
@@ -513,7 +529,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
         __syncthreads();
         ticket_to_unit(s_ticket, A.nb, ch, k);
     } else {
-        ch = blockIdx.x;
+        ch = xcd_channel(blockIdx.x, A.channels);
         k = 0;
     }
     if (ch >= A.channels) return;
@@ -535,7 +551,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
 #pragma unroll
         for (int c = 0; c < S; ++c) {
             float tmp[K];
-            load_steps<K, false>(A.s[c], soff, t0, T, A.s_vec != 0, tmp);
+            load_steps<K, false>(A.s[c], soff, t0, T, A.sst, A.s_vec != 0, tmp);
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) vset(s[kk], c, tmp[kk]);
         }
@@ -547,7 +563,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
             else if (t0 == tb0)
                 x = A.hin0[unit * S + c];
             else if (t0 - 1 < T)
-                x = A.s[c][soff + t0 - 1];
+                x = A.s[c][soff + (t0 - 1) * A.sst];
             vset(hin, c, x);
         }
     } else {
@@ -585,7 +601,8 @@ __global__ void solve_init_kernel(SolveArgs A, int32_t S, int64_t units, int32_t
             const int32_t k = (int32_t)(i - ch * A.nb);
             const int64_t b = ch / A.D, d = ch - b * A.D;
             for (int c = 0; c < S; ++c)
-                A.hin0[i * S + c] = k > 0 ? A.s[c][b * A.ssb + d * A.ssd + (int64_t)k * P - 1] : 0.0f;
+                A.hin0[i * S + c] =
+                    k > 0 ? A.s[c][b * A.ssb + d * A.ssd + ((int64_t)k * P - 1) * A.sst] : 0.0f;
         }
     }
 }

@@ -34,7 +34,8 @@ class PararnnError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("u_stride_b", ctypes.c_int64), ("u_stride_d", ctypes.c_int64),
-                ("s_stride_b", ctypes.c_int64), ("s_stride_d", ctypes.c_int64)]
+                ("s_stride_b", ctypes.c_int64), ("s_stride_d", ctypes.c_int64),
+                ("u_stride_t", ctypes.c_int64), ("s_stride_t", ctypes.c_int64)]
 
 
 class ProjShape(ctypes.Structure):
@@ -114,28 +115,48 @@ def _ptr_array(ts):
 
 
 def _strides(planes, name):
+    """Shared (stride_b, stride_d, stride_t) of planes indexed [B][D][T], or
+    None when every plane is empty.  Any layout is passed on (the library
+    rejects overlapping ones): channel-major [B][D][T] is the fast one, a
+    time-major [B][T][D] tensor is passed as its ``transpose(1, 2)`` view."""
     st = None
     for p in planes:
         if p is None:
             continue
         if p.dim() != 3:
-            raise ValueError(f"{name}: planes must be [B][D][T]")
+            raise ValueError(f"{name}: planes must be indexed [B][D][T]")
         if p.numel() == 0:
             continue
-        if p.stride(2) != 1:
-            raise ValueError(f"{name}: planes must be [B][D][T] with time contiguous")
-        s = (p.stride(0), p.stride(1))
+        s = tuple(p.stride())
         if st is not None and s != st:
             raise ValueError(f"{name}: all planes must share strides")
         st = s
     return st
 
 
+def _dense(B, T, D, like=None):
+    """Strides of a new plane: time-major when `like` (strides) is not
+    time-contiguous, channel-major otherwise."""
+    if like is not None and like[2] != 1 and T > 1:
+        return (T * D, 1, D)
+    return (D * T, T, 1)
+
+
+def _new_planes(n, B, T, D, like, dev):
+    st = _dense(B, T, D, like)
+    return [torch.empty_strided((B, D, T), st, dtype=torch.float32, device=dev)
+            for _ in range(n)]
+
+
 def make_shape(B, T, D, u_strides=None, s_strides=None):
-    """Shape record; strides default to dense [B][D][T]."""
-    us = u_strides or (D * T, T)
-    ss = s_strides or (D * T, T)
-    return Shape(B, T, D, us[0], us[1], ss[0], ss[1])
+    """Shape record; strides default to dense channel-major [B][D][T]."""
+    us = u_strides or (D * T, T, 1)
+    ss = s_strides or (D * T, T, 1)
+    if len(us) == 2:
+        us = (us[0], us[1], 1)
+    if len(ss) == 2:
+        ss = (ss[0], ss[1], 1)
+    return Shape(B, T, D, us[0], us[1], ss[0], ss[1], us[2], ss[2])
 
 
 def make_newton(tol=1e-6, max_iters=20, steps_per_lane=0, waves_per_block=0,
@@ -210,7 +231,7 @@ def _solve(cell, u, a, s0, out, tol, max_iters, steps_per_lane, waves_per_block,
     B, D, T = u[0].shape
     dev = u[0].device
     if out is None:
-        out = [torch.empty((B, D, T), dtype=torch.float32, device=dev) for _ in range(S)]
+        out = _new_planes(S, B, T, D, _strides(u, "u"), dev)
         if init_from_output:
             raise ValueError("init_from_output needs the output planes")
     shape = make_shape(B, T, D, _strides(u, "u"), _strides(out, "states"))
@@ -271,12 +292,12 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
         raise ValueError("wrong number of gate or state planes")
     B, D, T = u[0].shape
     dev = u[0].device
-    us = _strides(u, "u") or (D * T, T)
-    ss = _strides(s + [g for g in gs if g is not None], "states") or (D * T, T)
+    us = _strides(u, "u") or (D * T, T, 1)
+    ss = _strides(s + [g for g in gs if g is not None], "states") or (D * T, T, 1)
     if out is not None:
         du, da, ds0, lam = list(out["du"]), out["da"], list(out["ds0"]), out.get("lam")
         lam = list(lam) if (lam is not None and with_lambda) else None
-        dense = (D * T, T)
+        dense = (D * T, T, 1)
         if (len(du) != G or len(ds0) != S or tuple(da.shape) != (G, D)
                 or any(tuple(x.shape) != (B, D, T) for x in du + (lam or []))
                 or (_strides(du, "du") or dense) != us
@@ -291,12 +312,12 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
             if not x.is_contiguous():
                 raise ValueError("da and ds0 outputs must be contiguous")
     else:
-        du = [torch.empty_strided((B, D, T), (us[0], us[1], 1), dtype=torch.float32,
-                                  device=dev) for _ in range(G)]
+        du = [torch.empty_strided((B, D, T), us, dtype=torch.float32, device=dev)
+              for _ in range(G)]
         da = torch.empty((G, D), dtype=torch.float32, device=dev)
         ds0 = [torch.empty((B, D), dtype=torch.float32, device=dev) for _ in range(S)]
-        lam = ([torch.empty_strided((B, D, T), (ss[0], ss[1], 1), dtype=torch.float32,
-                                    device=dev) for _ in range(S)] if with_lambda else None)
+        lam = ([torch.empty_strided((B, D, T), ss, dtype=torch.float32, device=dev)
+                for _ in range(S)] if with_lambda else None)
     shape = make_shape(B, T, D, us, ss)
     newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
     nws = workspace_bytes(cell, shape, newton, adjoint=True)
@@ -356,14 +377,14 @@ def sequential(cell, u, a, s0, *, out=None, stream=None):
         raise ValueError("wrong number of gate or state planes")
     B, D, T = u[0].shape
     dev = u[0].device
-    us = _strides(u, "u") or (D * T, T)
+    us = _strides(u, "u") or (D * T, T, 1)
     if out is None:
-        out = [torch.empty((B, D, T), dtype=torch.float32, device=dev) for _ in range(S)]
+        out = _new_planes(S, B, T, D, us, dev)
     out = list(out)
     if len(out) != S or any(tuple(x.shape) != (B, D, T) or x.dtype != torch.float32
                             for x in out):
         raise ValueError("out must be S float32 planes [B][D][T]")
-    ss = _strides(out, "states") or (D * T, T)
+    ss = _strides(out, "states") or (D * T, T, 1)
     for x in s0:
         if tuple(x.shape) != (B, D) or not x.is_contiguous() or x.dtype != torch.float32:
             raise ValueError("initial states must be contiguous float32 [B][D]")
@@ -386,10 +407,10 @@ def scan(A, b, x0=None, *, reverse=False, out=None, steps_per_lane=0, waves_per_
         raise ValueError("state size must be 1 or 2 (A has S*S planes, b has S)")
     B, D, T = b[0].shape
     dev = b[0].device
-    ins = _strides(A + b, "A/b") or (D * T, T)
+    ins = _strides(A + b, "A/b") or (D * T, T, 1)
     if out is None:
-        out = [torch.empty((B, D, T), dtype=torch.float32, device=dev) for _ in range(S)]
-    outs = _strides(out, "x") or (D * T, T)
+        out = _new_planes(S, B, T, D, ins, dev)
+    outs = _strides(out, "x") or (D * T, T, 1)
     shape = make_shape(B, T, D, ins, outs)
     newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
     nws = int(lib.pararnn_scan_workspace_bytes(S, ctypes.byref(shape), ctypes.byref(newton)))

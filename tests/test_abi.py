@@ -101,6 +101,34 @@ def test_scan_keeps_channels_in_one_workgroup_up_to_8192_steps():
                                             ctypes.byref(n)) == 0
 
 
+def test_plane_layouts_accepted_and_rejected():
+    """Any non-overlapping (stride_b, stride_d, stride_t) is a valid plane
+    layout: channel-major, time-major [B][T][D], interleaved gate blocks of a
+    [B][T][G*D] tensor, padded and permuted ones; overlapping ones are
+    rejected before any device work."""
+    def ok(us, ss=None, B=2, T=16, D=3):
+        try:
+            pr.plan("gru", pr.make_shape(B, T, D, us, ss))
+            return True
+        except pr.PararnnError as e:
+            assert e.status == 1
+            return False
+
+    assert ok((48, 16, 1))                       # channel-major
+    assert ok((48, 1, 3), (48, 1, 3))            # time-major [B][T][D]
+    assert ok((144, 1, 9))                       # a gate block of [B][T][3*D]
+    assert ok((100, 1, 5))                       # padded rows
+    assert ok((1, 32, 2))                        # b fastest, then t, then d
+    assert ok((0, 16, 1), B=1)                   # extent-1 dimensions are free
+    assert ok((48, 1, 3), T=1, D=3)
+    assert not ok((48, 1, 2))                    # steps overlap channels
+    assert not ok((47, 1, 3))                    # batch rows overlap
+    assert not ok((48, 16, 0))                   # every step at one address
+    assert not ok((48, 1, 3), (48, 3, 1))        # the states' d and t overlap
+    assert not ok((48, 16, -1))
+    assert not ok((2 ** 62 + 16, 2 ** 61, 1))    # offsets past int64
+
+
 def _call_gru(shape, newton, u=(1, 1, 1), a=1, h0=1, h=1, ws=None, nws=0):
     lib = pr.load()
     arr = (ctypes.c_void_p * 3)(*[x or None for x in u])
