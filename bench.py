@@ -189,6 +189,80 @@ def bench_project(w, args):
     }, **extra)
 
 
+def bench_checkpoint(w, args):
+    """Training step (forward solve + backward through torch.autograd) on
+    the workload, one-piece vs checkpointed in time chunks of --chunk steps:
+    time per step and the peak device memory each holds beyond the inputs."""
+    import numpy as np
+    import torch
+    from nonlinear_rnn_amd import autograd as pag
+    from nonlinear_rnn_amd import longseq
+    from nonlinear_rnn_amd.inputs import workload_inputs
+
+    dev = "cuda:0"
+    inp = workload_inputs(w)
+    if inp.u_bf16 is not None:
+        u = [torch.from_numpy(p.view(np.int16)).view(torch.bfloat16).to(dev)
+             for p in inp.u_bf16]
+    else:
+        u = [torch.from_numpy(p).to(dev) for p in inp.u]
+    for p in u:
+        p.requires_grad_(True)
+    a = torch.from_numpy(inp.a).to(dev).requires_grad_(True)
+    s0 = [torch.from_numpy(p).to(dev).requires_grad_(True) for p in inp.s0]
+    rng = np.random.default_rng(w.seed + 7)
+    gh = torch.from_numpy(rng.standard_normal((w.B, w.D, w.T)).astype(np.float32)).to(dev)
+    del inp
+
+    def step(kind, held=None):
+        # the loss consumes the states and drops them, as a next layer would:
+        # what stays allocated until the backward is what the solve keeps
+        kw = dict(tol=w.tol, max_iters=w.max_iters)
+        if kind == "full":
+            out = pag.gru(u, a, s0[0], **kw) if w.cell == "gru" else pag.lstm(u, a, *s0, **kw)
+        elif w.cell == "gru":
+            out = longseq.gru_checkpointed(u, a, s0[0], chunk=args.chunk, **kw)
+        else:
+            out = longseq.lstm_checkpointed(u, a, *s0, chunk=args.chunk, **kw)
+        h = out if w.cell == "gru" else out[1]
+        loss = (h * gh).sum()
+        del out, h
+        if held is not None:
+            torch.cuda.synchronize()
+            held.append(torch.cuda.memory_allocated())
+        loss.backward()
+        for t in u + [a] + s0:
+            t.grad = None
+
+    res = {}
+    for kind in ("full", "checkpointed"):
+        for _ in range(args.warmup):
+            step(kind)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        held = []
+        step(kind, held)
+        torch.cuda.reset_peak_memory_stats()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(kind)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        res[kind] = {"ms_per_step": ms, "held_for_backward_bytes": held[0] - base,
+                     "peak_extra_bytes": torch.cuda.max_memory_allocated() - base}
+    return {
+        "metric": "training step (solve + adjoint) time and peak memory, one-piece vs "
+                  "checkpointed",
+        "value": w.N / (res["checkpointed"]["ms_per_step"] * 1e-3), "unit": "elem/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": res["checkpointed"]["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": data_recipe(w),
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "chunk": args.chunk},
+        "full": res["full"], "checkpointed": res["checkpointed"],
+        "state_bytes": w.S * w.B * w.D * w.T * 4,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,9 +270,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gru_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["solve", "project"], default="solve",
+    ap.add_argument("--op", choices=["solve", "project", "checkpoint"], default="solve",
                     help="solve: the Newton solve (default); project: the input projection "
-                         "u = W x + b for the workload's shapes with I = D inputs")
+                         "u = W x + b for the workload's shapes with I = D inputs; "
+                         "checkpoint: a training step one-piece vs checkpointed in time "
+                         "chunks (--chunk)")
+    ap.add_argument("--chunk", type=int, default=512,
+                    help="time chunk of --op checkpoint")
     ap.add_argument("--layout", choices=["channel", "time"], default="channel",
                     help="channel: [B][D][T] planes (default); time: the gate blocks of one "
                          "[B][T][G*D] projection tensor and [B][T][D] states")
@@ -222,6 +300,9 @@ def main():
     w = WORKLOADS[args.workload]
     if args.op == "project":
         print(json.dumps(bench_project(w, args)), flush=True)
+        return
+    if args.op == "checkpoint":
+        print(json.dumps(bench_checkpoint(w, args)), flush=True)
         return
     inp = workload_inputs(w)
     dev = "cuda:0"
