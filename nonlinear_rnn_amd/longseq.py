@@ -2,8 +2,8 @@
 
 Training keeps every hidden state of the sequence for the Newton iterations
 and for the backward pass, which for very long sequences dominates memory
-(the comparison of ParaRNN with Transformers and Mamba2 on the 53ai.com page,
-"长序列处理").  Two policies, both running every step in the HIP kernels of
+("ParaRNN：解锁非线性RNN并行训练的革命性框架", zhichai.net, section
+"性能对比：与Transformer和Mamba2的较量", item "长序列处理").  Two policies, both running every step in the HIP kernels of
 ``pararnn``; this module only orders the calls:
 
 * ``solve_chunked`` — the sequence is cut into time chunks solved one after
