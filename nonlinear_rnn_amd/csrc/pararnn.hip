@@ -417,14 +417,9 @@ pararnn_status_t pararnn_project(const pararnn_proj_shape_t *sh, const void *x, 
     A.usb = sh->u_stride_b;
     A.usm = sh->u_stride_m;
     A.out_bf16 = u_dtype == PARARNN_BF16 ? 1 : 0;
+    // workgroup count with the narrowest tile any projection kernel uses
     const int64_t tm = (sh->M + proj::kBM - 1) / proj::kBM, tn = (sh->T + proj::kBN - 1) / proj::kBN;
     if (tm * tn * sh->B >= (int64_t(1) << 31)) return PARARNN_ERR_UNSUPPORTED;
-    A.tiles_m = (int32_t)tm;
-    A.tiles_n = (int32_t)tn;
-    // m tiles per group: their W tiles (256 rows x I) together about 2 MB
-    const int64_t wtile = (int64_t)proj::kBM * sh->I * 2;
-    int64_t gm = wtile > 0 ? (int64_t(2) << 20) / wtile : tm;
-    A.group_m = (int32_t)(gm < 1 ? 1 : gm > tm ? tm : gm);
     const hipError_t e = launch_project(static_cast<hipStream_t>(stream), A);
     return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
 }

@@ -12,14 +12,17 @@
 // starts at row g*D).  bf16 operands, fp32 accumulation on the matrix cores
 // (v_mfma_f32_32x32x16_bf16), fp32 or bf16 (round to nearest even) output.
 //
-// Tiling: a 256-thread workgroup computes a 256 (m) x 128 (t) tile; each of
-// its 4 waves a 128 x 64 tile as 4 x 2 MFMA 32x32 blocks (128 accumulator
-// VGPRs).  K advances 32 at a time through two LDS stages: while the waves
-// multiply out of one stage, the next stage is in flight from memory into
-// registers and is written to the other one afterwards (one barrier per
-// step).  Tiles are ordered per XCD and in groups of m tiles so
-// that the workgroups in flight on one XCD share their operands in its L2.  LDS rows are padded to 80 bytes so the 16-byte operand
-// reads of 16 lanes cover all 64 banks once.
+// Two kernels.  Aligned operands (I % 64 == 0, 16-byte aligned rows) take
+// the ring kernel: a 512-thread workgroup computes a 256 (m) x 256 (t) tile,
+// each of its 8 waves a 128 x 64 tile as 4 x 2 MFMA 32x32 blocks; operand
+// tiles stream from memory straight into LDS (16-byte global->LDS copies,
+// whole 128-byte rows per k step of 64: the copy path runs at half rate on
+// half lines) through a 2-stage ring, rows XOR-swizzled so the 16-byte
+// operand reads are bank-conflict free.  Anything else takes the register-
+// staged kernel: 256 x 128 tiles, k steps of 32 through two padded LDS
+// stages, per-element checked loads.  Both order tiles per XCD and in groups
+// of m tiles so that the workgroups in flight on one XCD share their
+// operands in its L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,10 +45,18 @@ struct ProjArgs {
 
 namespace proj {
 
+#ifndef PARARNN_PROJ_BN
+#define PARARNN_PROJ_BN 128
+#endif
 #ifndef PARARNN_PROJ_BK
 #define PARARNN_PROJ_BK 32
 #endif
-constexpr int kBM = 256, kBN = 128, kBK = PARARNN_PROJ_BK;
+#ifndef PARARNN_PROJ_OCC
+#define PARARNN_PROJ_OCC 2
+#endif
+constexpr int kBM = 256, kBN = PARARNN_PROJ_BN, kBK = PARARNN_PROJ_BK;
+constexpr int kWM = kBM / 2, kWN = kBN / 2;  // wave tile (2 x 2 waves)
+constexpr int kMB = kWM / 32, kNB = kWN / 32;  // 32x32 MFMA blocks per wave
 constexpr int kRow = kBK + 8;   // padded LDS row, bf16 elements
 constexpr int kCR = kBK / 8;    // 16-byte chunks per row
 constexpr int kThreads = 256;
@@ -74,6 +85,77 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t *row, int64_t k, int6
     return v;
 }
 
+// ---- direct-to-LDS ring (aligned operands)
+// A stage holds the A tile (kBM rows) then the B tile (kBN rows), each row
+// kBK bf16 = kCR 16-byte chunks, unpadded; chunk c of row r sits at chunk
+// position c ^ swz(r), so the 16-byte operand reads of 8 (or 16) consecutive
+// lanes — 8 (16) consecutive rows at one chunk — fall on distinct banks.
+#ifndef PARARNN_PROJ_RING_BN
+#define PARARNN_PROJ_RING_BN 256
+#endif
+#ifndef PARARNN_PROJ_RING_BK
+#define PARARNN_PROJ_RING_BK 64
+#endif
+#ifndef PARARNN_PROJ_RING_WAVES
+#define PARARNN_PROJ_RING_WAVES 8
+#endif
+#ifndef PARARNN_PROJ_RING_WM
+#define PARARNN_PROJ_RING_WM 2
+#endif
+#ifndef PARARNN_PROJ_RING_STAGES
+#define PARARNN_PROJ_RING_STAGES 2
+#endif
+#ifndef PARARNN_PROJ_RING_OCC
+#define PARARNN_PROJ_RING_OCC 2
+#endif
+constexpr int kRBN = PARARNN_PROJ_RING_BN, kRBK = PARARNN_PROJ_RING_BK;
+constexpr int kRWaves = PARARNN_PROJ_RING_WAVES, kRThreads = 64 * kRWaves;
+constexpr int kRWMw = PARARNN_PROJ_RING_WM, kRWNw = kRWaves / kRWMw;  // wave grid
+constexpr int kRWM = kBM / kRWMw, kRWN = kRBN / kRWNw;              // wave tile
+constexpr int kRMB = kRWM / 32, kRNB = kRWN / 32;                    // MFMA blocks
+constexpr int kStages = PARARNN_PROJ_RING_STAGES;
+constexpr int kRCR = kRBK / 8;                                        // chunks per row
+constexpr int kRowBytes = kRBK * 2;
+constexpr int kAStage = kBM * kRowBytes, kStageBytes = (kBM + kRBN) * kRowBytes;
+constexpr int kAQ = kBM * kRCR / 64 / kRWaves, kBQ = kRBN * kRCR / 64 / kRWaves;  // copies per wave
+constexpr int kPerStage = kAQ + kBQ;
+static_assert(kAQ * 64 * kRWaves == kBM * kRCR && kBQ * 64 * kRWaves == kRBN * kRCR,
+              "stage must split evenly into 1 KB copies");
+static_assert(kRMB >= 1 && kRNB >= 1 && (kStages - 2) * kPerStage < 64, "ring shape");
+// Chunk position of memory chunk c in tile row r: c ^ swz(r).  16-byte reads
+// of 8 (or 16) consecutive rows at one chunk then hit distinct banks.
+__device__ __forceinline__ int swz(int r)
+{
+    if constexpr (kRCR == 8)
+        return (r ^ (r >> 3)) & 7;
+    else
+        return ((r >> 1) ^ (r >> 2)) & 3;
+}
+
+// A wave-uniform pointer, moved to scalar registers (the asm below takes its
+// base address in an SGPR pair).
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void copy_to_lds(uint32_t voff, const void *sbase, uint32_t lds)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory");
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
     uint32_t u = __float_as_uint(f);
@@ -89,7 +171,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 // chunk of every stage lies inside its row: unconditional vector loads (rows
 // past M or T read a valid row whose results are not stored).
 template <bool VEC>
-__global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
+__global__ void __launch_bounds__(proj::kThreads, PARARNN_PROJ_OCC) project_kernel(ProjArgs A)
 {
     using namespace proj;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM][kRow];
@@ -116,7 +198,7 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*128, cols wn*64
+    const int wm = wave >> 1, wn = wave & 1;  // wave tile: rows wm*kWM, cols wn*kWN
     const int64_t K = A.I;
     const uint16_t *xb = A.x + b * A.xsb;
     const bool wvec = (A.wsm % 8 == 0) && ((reinterpret_cast<uintptr_t>(A.w) & 15u) == 0);
@@ -166,11 +248,11 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
         }                                                                                       \
     } while (0)
 
-    f32x16 acc[4][2];
+    f32x16 acc[kMB][kNB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kMB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kNB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -179,19 +261,19 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
     auto mma = [&](int buf) {
 #pragma unroll
         for (int h = 0; h < kBK / 16; ++h) {
-            bf16x8 fa[4], fb[2];
+            bf16x8 fa[kMB], fb[kNB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kMB; ++i)
                 fa[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &As[buf][wm * 128 + i * 32 + ar][h * 16 + ak]));
+                    &As[buf][wm * kWM + i * 32 + ar][h * 16 + ak]));
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < kNB; ++j)
                 fb[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &Bs[buf][wn * 64 + j * 32 + ar][h * 16 + ak]));
+                    &Bs[buf][wn * kWN + j * 32 + ar][h * 16 + ak]));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kMB; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kNB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
                                                                         0, 0, 0);
         }
@@ -218,19 +300,170 @@ __global__ void __launch_bounds__(proj::kThreads, 2) project_kernel(ProjArgs A)
 
     // epilogue: accumulator r of block (i, j) holds row
     // 8 (r / 4) + 4 (lane / 32) + r % 4 and column lane % 32 of that block
-    const int64_t col_base = n0 + wn * 64 + (lane & 31);
+    const int64_t col_base = n0 + wn * kWN + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kMB; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int64_t m = m0 + wm * kWM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             if (m >= A.M) continue;
             const float bias = A.bias ? A.bias[m] : 0.0f;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kNB; ++j) {
                 const int64_t t = col_base + j * 32;
                 if (t >= A.T) continue;
                 const float v = acc[i][j][r] + bias;
+                const int64_t off = b * A.usb + m * A.usm + t;
+                if (A.out_bf16)
+                    static_cast<uint16_t *>(A.u)[off] = f32_to_bf16_rne(v);
+                else
+                    static_cast<float *>(A.u)[off] = v;
+            }
+        }
+    }
+}
+
+// Aligned operands (I % kRBK == 0, 16-byte aligned rows): tiles stream
+// straight into a ring of kStages LDS stages; while stage s is multiplied,
+// stages s + 1 .. s + kStages - 1 are in flight, one barrier per step.  Each
+// copy moves whole 128-byte rows when kRBK = 64 (the load path runs at half
+// rate on half lines).
+__global__ void __launch_bounds__(proj::kRThreads, PARARNN_PROJ_RING_OCC)
+    project_kernel_ring(ProjArgs A)
+{
+    using namespace proj;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages][kStageBytes];
+
+    const int64_t total = (int64_t)A.tiles_m * A.tiles_n * A.B;
+    int64_t g = blockIdx.x;
+    if (total % 8 == 0) g = (g % 8) * (total / 8) + g / 8;
+    const int64_t per_b = (int64_t)A.tiles_m * A.tiles_n;
+    const int64_t b = g / per_b;
+    const int64_t r = g - b * per_b;
+    const int64_t mg = r / ((int64_t)A.group_m * A.tiles_n);
+    const int64_t gsz = (A.tiles_m - mg * A.group_m) < A.group_m ? (A.tiles_m - mg * A.group_m)
+                                                                  : A.group_m;
+    const int64_t rr = r - mg * A.group_m * A.tiles_n;
+    const int64_t tn = rr / gsz;
+    const int64_t tm = mg * A.group_m + (rr - tn * gsz);
+    const int64_t m0 = tm * kBM, n0 = tn * kRBN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / kRWNw, wn = wave % kRWNw;
+    const int64_t K = A.I;
+    const int steps = (int)(K / kRBK);
+
+    // copy plan: copy q of this wave fills 1 KB block q * kRWaves + wave of
+    // the A (then B) tile; lane l of it takes chunk position p = 64 block + l,
+    // i.e. tile row p / kRCR and memory chunk (p % kRCR) ^ swz(row).  Rows
+    // past M or T read the last row (their results are not stored).
+    const uint8_t *wbase = uniform_ptr(reinterpret_cast<const uint8_t *>(A.w + m0 * A.wsm));
+    const uint8_t *xbase =
+        uniform_ptr(reinterpret_cast<const uint8_t *>(A.x + b * A.xsb + n0 * A.xst));
+    uint32_t voa[kAQ], vob[kBQ];
+#pragma unroll
+    for (int q = 0; q < kAQ; ++q) {
+        const int p = (q * kRWaves + wave) * 64 + lane, row = p / kRCR;
+        const int64_t m = m0 + row < A.M ? m0 + row : A.M - 1;
+        voa[q] = (uint32_t)(((m - m0) * A.wsm + ((p % kRCR) ^ swz(row)) * 8) * 2);
+    }
+#pragma unroll
+    for (int q = 0; q < kBQ; ++q) {
+        const int p = (q * kRWaves + wave) * 64 + lane, row = p / kRCR;
+        const int64_t t = n0 + row < A.T ? n0 + row : A.T - 1;
+        vob[q] = (uint32_t)(((t - n0) * A.xst + ((p % kRCR) ^ swz(row)) * 8) * 2);
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)reinterpret_cast<uintptr_t>(&ring[0][0]) + wave * 1024);
+    auto issue = [&](int s) {
+        const uint32_t l = lds0 + (uint32_t)((s % kStages) * kStageBytes);
+        const int64_t kb = (int64_t)s * kRowBytes;
+#pragma unroll
+        for (int q = 0; q < kAQ; ++q) copy_to_lds(voa[q], wbase + kb, l + q * kRWaves * 1024);
+#pragma unroll
+        for (int q = 0; q < kBQ; ++q)
+            copy_to_lds(vob[q], xbase + kb, l + kAStage + q * kRWaves * 1024);
+    };
+
+    f32x16 acc[kRMB][kRNB];
+#pragma unroll
+    for (int i = 0; i < kRMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kRNB; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // operand row of this lane in block i (j): base + 32 i + lane % 32; the
+    // k16 step h reads memory chunk 2 h + lane / 32 of it
+    const int lr = lane & 31, lh = lane >> 5;
+    auto a_off = [&](int i, int h) {
+        const int row = wm * kRWM + i * 32 + lr;
+        return row * kRowBytes + (((2 * h + lh) ^ swz(row)) * 16);
+    };
+    auto b_off = [&](int j, int h) {
+        const int row = wn * kRWN + j * 32 + lr;
+        return kAStage + row * kRowBytes + (((2 * h + lh) ^ swz(row)) * 16);
+    };
+
+    for (int s = 0; s < kStages - 1 && s < steps; ++s) issue(s);
+    for (int s = 0; s < steps; ++s) {
+        // this wave's copies of stage s have landed (later stages may fly)
+        if (kStages > 2 && s + kStages - 2 < steps)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | ((kStages - 2) * kPerStage & 15) |
+                                       (((kStages - 2) * kPerStage >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_s_barrier();  // all copies of stage s landed; stage s - 1 is free
+        asm volatile("" ::: "memory");
+        if (s + kStages - 1 < steps) issue(s + kStages - 1);
+        const uint8_t *st = &ring[s % kStages][0];
+#ifndef PARARNN_PROJ_RING_AHEAD
+#define PARARNN_PROJ_RING_AHEAD 2
+#endif
+        // operand reads of PARARNN_PROJ_RING_AHEAD k16 steps first, then
+        // their products: the first products wait only for their own operands
+        constexpr int kAh = PARARNN_PROJ_RING_AHEAD;
+#pragma unroll
+        for (int h2 = 0; h2 < kRBK / 16 / kAh; ++h2) {
+            bf16x8 fa[kAh][kRMB], fb[kAh][kRNB];
+#pragma unroll
+            for (int hh = 0; hh < kAh; ++hh) {
+#pragma unroll
+                for (int i = 0; i < kRMB; ++i)
+                    fa[hh][i] = as_bf16x8(
+                        *reinterpret_cast<const uint4 *>(st + a_off(i, kAh * h2 + hh)));
+#pragma unroll
+                for (int j = 0; j < kRNB; ++j)
+                    fb[hh][j] = as_bf16x8(
+                        *reinterpret_cast<const uint4 *>(st + b_off(j, kAh * h2 + hh)));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int hh = 0; hh < kAh; ++hh)
+#pragma unroll
+                for (int i = 0; i < kRMB; ++i)
+#pragma unroll
+                    for (int j = 0; j < kRNB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            fa[hh][i], fb[hh][j], acc[i][j], 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");
+    }
+
+    const int64_t col_base = n0 + wn * kRWN + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < kRMB; ++i) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t m = m0 + wm * kRWM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m >= A.M) continue;
+            const float bias = A.bias ? A.bias[m] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < kRNB; ++j) {
+                const int64_t t = col_base + j * 32;
+                if (t >= A.T) continue;
+                const float v = acc[i][j][e] + bias;
                 const int64_t off = b * A.usb + m * A.usm + t;
                 if (A.out_bf16)
                     static_cast<uint16_t *>(A.u)[off] = f32_to_bf16_rne(v);
