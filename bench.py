@@ -162,6 +162,24 @@ def bench_project(w, args):
     ob = 2 if out_dtype == torch.bfloat16 else 4
     nbytes = w.B * w.T * I * 2 + M * I * 2 + M * 4 + w.B * M * w.T * ob
     extra = {}
+    # context: the library GEMM (hipBLASLt through torch.matmul) on the same
+    # bf16 operands with bf16 output; the right operand is made contiguous
+    # (x^T per batch row) outside the timed region
+    xt = x.transpose(1, 2).contiguous()
+    for _ in range(args.warmup):
+        torch.matmul(wt, xt)
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in lev:
+        e0.record(stream)
+        torch.matmul(wt, xt)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    lms = sorted(e0.elapsed_time(e1) for e0, e1 in lev)[len(lev) // 2]
+    extra["library_gemm"] = {"tflops": flops / (lms * 1e-3) / 1e12, "ms": lms,
+                             "kind": "torch.matmul (hipBLASLt), same bf16 operands, bf16 "
+                                     "output, no bias; context, not a baseline"}
+    del xt
     if args.copy_mib:
         n = args.copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
