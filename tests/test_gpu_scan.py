@@ -62,6 +62,15 @@ def test_scan_without_boundary_value(S):
     assert np.abs(got - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
 
 
+@pytest.mark.parametrize("S", [1, 2])
+def test_scan_empty(S):
+    """No steps, no batch rows or no channels: nothing to do, no error."""
+    for B, T, D in [(0, 10, 3), (2, 0, 3), (2, 10, 0)]:
+        A, b, x0 = make(S, B, T, D, 812)
+        got = run(A, b, x0, False)
+        assert got.shape == (S, B, D, T)
+
+
 def test_scan_is_the_newton_system():
     """One Newton update of the fused solve equals a scan of its own
     Jacobians and residuals: from s = 0 with one update, s^(1) = ds solves

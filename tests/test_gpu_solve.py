@@ -150,6 +150,16 @@ def test_empty_problems():
         assert info["converged"] and info["iters"] == 0
 
 
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_channels_along_batch_only(cell):
+    """D = 1: every channel is a batch row (257 of them, not a multiple of the
+    8 XCDs, so some workgroups of the grid have no channel)."""
+    inp = make_inputs(cell, 257, 300, 1, 4600, s0_std=0.2, f_bias=1.0)
+    got, info = gpu_solve(inp, 1e-6, 30)
+    assert info["converged"] and info["units"] == 257
+    assert max_err(got, oracle_states(inp)) < TOL32
+
+
 def test_strided_planes():
     """Planes that are views of larger buffers (row strides > T, not 16-byte
     multiples) take the scalar load path and give the same answer."""
