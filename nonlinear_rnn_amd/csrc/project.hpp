@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace pararnn {
 
@@ -156,17 +157,82 @@ __device__ __forceinline__ void copy_to_lds(uint32_t voff, const void *sbase, ui
         : "memory");
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
 
 }  // namespace proj
 
 #ifdef PARARNN_DEFINE_PROJECT_KERNEL  // compiled once, in its own translation unit
+// Epilogue rows: accumulator e of block (i, j) holds row
+// 8 (e / 4) + 4 (lane / 32) + e % 4 and column lane % 32 of that block, so
+// this lane writes rows mrow0 + 32 i + 8 g + r (g, r < 4) at columns
+// tcol0 + 32 j.  FULL: the tile lies inside M x T (no per-element checks).
+template <bool BF16OUT, bool FULL>
+__device__ __forceinline__ void store_rows(const ProjArgs &A, int64_t b, int64_t mrow0,
+                                           int64_t tcol0,
+                                           const proj::f32x16 (&acc)[proj::kRMB][proj::kRNB],
+                                           const float (&bias)[proj::kRMB][4][4])
+{
+    using namespace proj;
+    using Out = typename std::conditional<BF16OUT, __bf16, float>::type;
+    Out *u = static_cast<Out *>(A.u) + b * A.usb + tcol0;
+#pragma unroll
+    for (int i = 0; i < kRMB; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = mrow0 + i * 32 + 8 * g + r;
+                if (!FULL && m >= A.M) continue;
+                Out *row = u + m * A.usm;
+#pragma unroll
+                for (int j = 0; j < kRNB; ++j) {
+                    if (!FULL && tcol0 + j * 32 >= A.T) continue;
+                    row[j * 32] = (Out)(acc[i][j][4 * g + r] + bias[i][g][r]);
+                }
+            }
+}
+
+// Epilogue of both kernels (their waves hold the same 128 x 64 tile shape):
+// bias, then fp32 or bf16 (the hardware's round-to-nearest-even conversion)
+// stores.  full_m / full: the tile's rows / rows and columns all exist.
+__device__ __forceinline__ void store_tile(const ProjArgs &A, int64_t b, int64_t mrow0,
+                                           int64_t tcol0, bool full, bool full_m,
+                                           const proj::f32x16 (&acc)[proj::kRMB][proj::kRNB])
+{
+    using namespace proj;
+    // bias of this lane's rows: four consecutive rows per 16-byte load when
+    // the tile's rows all exist and the bias array is 16-byte aligned
+    float bias[kRMB][4][4];
+    const bool bvec = full_m && (reinterpret_cast<uintptr_t>(A.bias) & 15u) == 0;
+#pragma unroll
+    for (int i = 0; i < kRMB; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int64_t m = mrow0 + i * 32 + 8 * g;
+            if (A.bias && bvec) {
+                const float4 v = *reinterpret_cast<const float4 *>(A.bias + m);
+                bias[i][g][0] = v.x;
+                bias[i][g][1] = v.y;
+                bias[i][g][2] = v.z;
+                bias[i][g][3] = v.w;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    bias[i][g][r] = (A.bias && m + r < A.M) ? A.bias[m + r] : 0.0f;
+            }
+        }
+    if (A.out_bf16) {
+        if (full)
+            store_rows<true, true>(A, b, mrow0, tcol0, acc, bias);
+        else
+            store_rows<true, false>(A, b, mrow0, tcol0, acc, bias);
+    } else {
+        if (full)
+            store_rows<false, true>(A, b, mrow0, tcol0, acc, bias);
+        else
+            store_rows<false, false>(A, b, mrow0, tcol0, acc, bias);
+    }
+}
+
 // VEC: every row of x and W is 16-byte aligned and I % 32 == 0, so every
 // chunk of every stage lies inside its row: unconditional vector loads (rows
 // past M or T read a valid row whose results are not stored).
@@ -298,29 +364,9 @@ __global__ void __launch_bounds__(proj::kThreads, PARARNN_PROJ_OCC) project_kern
 #undef PARARNN_PROJ_FETCH
 #undef PARARNN_PROJ_STASH
 
-    // epilogue: accumulator r of block (i, j) holds row
-    // 8 (r / 4) + 4 (lane / 32) + r % 4 and column lane % 32 of that block
-    const int64_t col_base = n0 + wn * kWN + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < kMB; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wm * kWM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m >= A.M) continue;
-            const float bias = A.bias ? A.bias[m] : 0.0f;
-#pragma unroll
-            for (int j = 0; j < kNB; ++j) {
-                const int64_t t = col_base + j * 32;
-                if (t >= A.T) continue;
-                const float v = acc[i][j][r] + bias;
-                const int64_t off = b * A.usb + m * A.usm + t;
-                if (A.out_bf16)
-                    static_cast<uint16_t *>(A.u)[off] = f32_to_bf16_rne(v);
-                else
-                    static_cast<float *>(A.u)[off] = v;
-            }
-        }
-    }
+    static_assert(kMB == kRMB && kNB == kRNB, "both kernels share the epilogue");
+    store_tile(A, b, m0 + wm * 128 + 4 * (lane >> 5), n0 + wn * 64 + (lane & 31),
+               m0 + kBM <= A.M && n0 + kBN <= A.T, m0 + kBM <= A.M, acc);
 }
 
 // Aligned operands (I % kRBK == 0, 16-byte aligned rows): tiles stream
@@ -451,27 +497,8 @@ __global__ void __launch_bounds__(proj::kRThreads, PARARNN_PROJ_RING_OCC)
         asm volatile("" ::: "memory");
     }
 
-    const int64_t col_base = n0 + wn * kRWN + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < kRMB; ++i) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t m = m0 + wm * kRWM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            if (m >= A.M) continue;
-            const float bias = A.bias ? A.bias[m] : 0.0f;
-#pragma unroll
-            for (int j = 0; j < kRNB; ++j) {
-                const int64_t t = col_base + j * 32;
-                if (t >= A.T) continue;
-                const float v = acc[i][j][e] + bias;
-                const int64_t off = b * A.usb + m * A.usm + t;
-                if (A.out_bf16)
-                    static_cast<uint16_t *>(A.u)[off] = f32_to_bf16_rne(v);
-                else
-                    static_cast<float *>(A.u)[off] = v;
-            }
-        }
-    }
+    store_tile(A, b, m0 + wm * kRWM + 4 * (lane >> 5), n0 + wn * kRWN + (lane & 31),
+               m0 + kBM <= A.M && n0 + kRBN <= A.T, m0 + kBM <= A.M, acc);
 }
 #endif
 
