@@ -67,12 +67,25 @@ def data_recipe(w):
     return f"synthetic (seeded numpy PCG64, seed {w.seed}: " + ", ".join(parts) + ")"
 
 
-def kernel_source_digest():
+# Sources whose code only the input projection uses; every other file under
+# csrc/ (and the ABI header) builds the solve, adjoint and scan kernels.
+PROJECTION_ONLY = ("project.hpp", "inst_project.hip")
+
+
+def kernel_source_digest(family="solve"):
+    """Hash of the sources a kernel family is built from: "project" (the
+    projection kernels and the ABI) or "solve" (everything else)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nonlinear_rnn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    names = sorted(os.listdir(csrc))
+    if family == "project":
+        names = [n for n in names if n in PROJECTION_ONLY or n == "pararnn.hip"]
+    else:
+        names = [n for n in names if n not in PROJECTION_ONLY]
+    paths = [os.path.join(csrc, n) for n in names] + [os.path.join(ROOT, "include", "pararnn.h")]
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + f.read())
     return h.hexdigest()[:16]
 
 
@@ -84,7 +97,8 @@ def measured_traffic(key):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_digest") != kernel_source_digest():
+    family = "project" if key.startswith("project_") else "solve"
+    if rec.get("kernel_source_digest") != kernel_source_digest(family):
         return None
     return rec.get("hbm_bytes_per_launch")
 
