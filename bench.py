@@ -295,6 +295,61 @@ def bench_checkpoint(w, args):
     }
 
 
+def bench_speedup(args):
+    """Parallel (Newton) vs sequential application on the same GPU, the
+    comparison behind the pages' speed-up figures: ParaGRU f32 with 64
+    channels (B=1, D=64, the small workload's width) and growing T, inputs
+    drawn as for that workload (seed 1).  Both kernels produce the same
+    trajectory (to the Newton tolerance); times are HIP-event medians."""
+    import numpy as np
+    import torch
+    from nonlinear_rnn_amd import pararnn as pr
+    from nonlinear_rnn_amd.inputs import make_inputs
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    points = []
+    for T in (1024, 4096, 16384, 65536, 262144):
+        inp = make_inputs("gru", 1, T, 64, 1)
+        u = [torch.from_numpy(p).to(dev) for p in inp.u]
+        a = torch.from_numpy(inp.a).to(dev)
+        h0 = torch.from_numpy(inp.s0[0]).to(dev)
+        h = torch.empty((1, 64, T), dtype=torch.float32, device=dev)
+        hs = [torch.empty_like(h)]
+
+        def newton():
+            pr.solve_gru(u, a, h0, out=h, tol=1e-6, max_iters=20, info=False, stream=stream)
+
+        def seq():
+            pr.sequential("gru", u, a, [h0], out=hs, stream=stream)
+
+        res = {}
+        for name, fn in (("newton", newton), ("sequential", seq)):
+            for _ in range(max(1, args.warmup)):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(7)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[3]
+        info = pr.read_info(pr.solve_gru(u, a, h0, out=h, tol=1e-6, max_iters=20)[1])
+        err = float((h - hs[0]).abs().max())
+        points.append({"T": T, "newton_ms": res["newton"], "sequential_ms": res["sequential"],
+                       "speedup": res["sequential"] / res["newton"],
+                       "newton_updates": info["iters"], "max_abs_diff": err})
+    best = max(points, key=lambda q: q["speedup"])
+    return {"metric": "parallel (Newton) vs sequential application, same GPU",
+            "value": best["speedup"], "unit": "x", "n_gpus": 1, "steps": 7,
+            "warmup": args.warmup, "ms_per_step": best["newton_ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded numpy PCG64, seed 1: u~N(0,1), a~U(-1,1), h0=0)",
+            "config": {"workload": "ParaGRU f32 B=1 D=64, T from 1024 to 262144"},
+            "points": points}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,11 +357,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gru_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=["solve", "project", "checkpoint"], default="solve",
+    ap.add_argument("--op", choices=["solve", "project", "checkpoint", "speedup"], default="solve",
                     help="solve: the Newton solve (default); project: the input projection "
                          "u = W x + b for the workload's shapes with I = D inputs; "
                          "checkpoint: a training step one-piece vs checkpointed in time "
-                         "chunks (--chunk)")
+                         "chunks (--chunk); speedup: Newton vs sequential application on "
+                         "the same GPU, 64 channels, growing T")
     ap.add_argument("--chunk", type=int, default=512,
                     help="time chunk of --op checkpoint")
     ap.add_argument("--layout", choices=["channel", "time"], default="channel",
@@ -335,6 +391,9 @@ def main():
         return
     if args.op == "checkpoint":
         print(json.dumps(bench_checkpoint(w, args)), flush=True)
+        return
+    if args.op == "speedup":
+        print(json.dumps(bench_speedup(args)), flush=True)
         return
     inp = workload_inputs(w)
     dev = "cuda:0"
