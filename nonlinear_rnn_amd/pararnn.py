@@ -189,18 +189,24 @@ def decode_info(raw) -> dict:
 
 
 class Workspace:
-    """Grow-only device scratch buffer (torch-allocated), one per device."""
+    """Grow-only device scratch buffers (torch-allocated), one per device
+    and stream: the kernels' per-launch state (tickets, flags, records,
+    partial sums) lives there, so launches on different streams must not
+    share one.  Each buffer is allocated on its own stream, so torch's
+    allocator orders its reuse after that stream's work."""
 
     def __init__(self):
         self.buf = {}
 
-    def get(self, nbytes, device):
+    def get(self, nbytes, device, stream=None):
         if nbytes == 0:
             return None
-        key = torch.device(device).index
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        key = (torch.device(device).index, s.cuda_stream)
         b = self.buf.get(key)
         if b is None or b.numel() < nbytes:
-            b = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            with torch.cuda.stream(s):
+                b = torch.empty(nbytes, dtype=torch.uint8, device=device)
             self.buf[key] = b
         return b
 
@@ -237,7 +243,7 @@ def _solve(cell, u, a, s0, out, tol, max_iters, steps_per_lane, waves_per_block,
     shape = make_shape(B, T, D, _strides(u, "u"), _strides(out, "states"))
     newton = make_newton(tol, max_iters, steps_per_lane, waves_per_block, init_from_output)
     nws = workspace_bytes(cell, shape, newton)
-    ws = workspace if workspace is not None else _ws.get(nws, dev)
+    ws = workspace if workspace is not None else _ws.get(nws, dev, stream)
     info_t = torch.empty(INFO_BYTES, dtype=torch.uint8, device=dev) if info else None
     args = [ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a)]
     args += [_ptr(x) for x in s0] + [_ptr(x) for x in out]
@@ -321,7 +327,7 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
     shape = make_shape(B, T, D, us, ss)
     newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
     nws = workspace_bytes(cell, shape, newton, adjoint=True)
-    ws = workspace if workspace is not None else _ws.get(nws, dev)
+    ws = workspace if workspace is not None else _ws.get(nws, dev, stream)
     _check(lib.pararnn_adjoint(cell, ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a),
                                _ptr_array(s0), _ptr_array(s), _ptr_array(gs), _ptr_array(du),
                                _ptr(da), _ptr_array(ds0),
@@ -414,7 +420,7 @@ def scan(A, b, x0=None, *, reverse=False, out=None, steps_per_lane=0, waves_per_
     shape = make_shape(B, T, D, ins, outs)
     newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
     nws = int(lib.pararnn_scan_workspace_bytes(S, ctypes.byref(shape), ctypes.byref(newton)))
-    ws = workspace if workspace is not None else _ws.get(nws, dev)
+    ws = workspace if workspace is not None else _ws.get(nws, dev, stream)
     _check(lib.pararnn_scan(S, ctypes.byref(shape), _ptr_array(A), _ptr_array(b),
                             _ptr_array(x0) if x0 is not None else None, _ptr_array(out),
                             1 if reverse else 0, ctypes.byref(newton), _ptr(ws),
