@@ -10,6 +10,7 @@
 #include "scan_kernel.hpp"
 #include "sequential.hpp"
 #include "solve.hpp"
+#include "transpose.hpp"
 
 namespace pararnn {
 

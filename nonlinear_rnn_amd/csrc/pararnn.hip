@@ -172,10 +172,10 @@ pararnn_status_t check_newton(const pararnn_newton_t *opt)
     return PARARNN_OK;
 }
 
-pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, const void *const *u,
-                              pararnn_dtype_t dt, const float *a, const float *const *s0,
-                              float *const *s, const pararnn_newton_t *opt, pararnn_info_t *info,
-                              void *ws, size_t ws_bytes, void *stream)
+pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, const void *const *u,
+                            pararnn_dtype_t dt, const float *a, const float *const *s0,
+                            float *const *s, const pararnn_newton_t *opt, pararnn_info_t *info,
+                            void *ws, size_t ws_bytes, void *stream)
 {
     pararnn_status_t st = check_newton(opt);
     if (st != PARARNN_OK) return st;
@@ -260,6 +260,151 @@ pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, co
         e = dt == PARARNN_BF16 ? launch_newton_lstm_bf16(pl.K, pl.W, variant, groups, strm, A)
                                : launch_newton_lstm_f32(pl.K, pl.W, variant, groups, strm, A);
     return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+}
+
+// ------------------------------------------------- time-major staging ---
+// Planes that are not time-contiguous (time-major [B][T][D] and the like)
+// are read by the solve with one 4-byte load per step.  With room in the
+// workspace they are staged instead: copied into channel-major scratch by
+// plane_transpose_kernel, solved there, and the states copied back.
+struct Stage {
+    bool u = false, s = false;
+    size_t u_off = 0, u_plane = 0, s_off = 0, s_plane = 0, total = 0;
+};
+
+Stage stage_layout(pararnn_cell_t cell, const pararnn_shape_t *sh, size_t u_esize, size_t base)
+{
+    Stage g;
+    if (!sh || sh->B <= 0 || sh->D <= 0 || sh->T <= 1) return g;
+    const int64_t n = sh->B * sh->D;
+    if (n > (int64_t(1) << 40) / sh->T) return g;  // no staging for absurd sizes
+    const int64_t e = n * sh->T;
+    g.u = sh->u_stride_t != 1;
+    g.s = sh->s_stride_t != 1;
+    if (!g.u && !g.s) return g;
+    size_t off = align_up(base);
+    if (g.u) {
+        g.u_off = off;
+        g.u_plane = align_up((size_t)e * u_esize);
+        off += (size_t)cell_G(cell) * g.u_plane;
+    }
+    if (g.s) {
+        g.s_off = off;
+        g.s_plane = align_up((size_t)e * sizeof(float));
+        off += (size_t)cell_S(cell) * g.s_plane;
+    }
+    g.total = off;
+    return g;
+}
+
+// Whether a plane with strides (sd, st) is walked faster along t than d.
+int32_t t_fast(int64_t sd, int64_t st) { return st == 1 ? 1 : sd == 1 ? 0 : (st <= sd ? 1 : 0); }
+
+hipError_t launch_transpose(int esize, const TransArgs &t, hipStream_t st)
+{
+    const int64_t groups = transpose_groups(t.B, t.T, t.D);
+    if (groups == 0) return hipSuccess;
+    if (esize == 2) {
+        TransArgs t2 = t;
+        t2.vec = 0;
+        hipLaunchKernelGGL(plane_transpose_kernel<2>, dim3((unsigned)groups), dim3(256), 0, st, t2);
+    } else {
+        hipLaunchKernelGGL(plane_transpose_kernel<4>, dim3((unsigned)groups), dim3(256), 0, st, t);
+    }
+    return hipGetLastError();
+}
+
+TransArgs plane_copy(const void *src, const pararnn_shape_t *sh, int64_t sb, int64_t sd, int64_t st,
+                     void *dst, int64_t db, int64_t dd, int64_t dt)
+{
+    TransArgs t;
+    t.src = src;
+    t.dst = dst;
+    t.B = sh->B;
+    t.T = sh->T;
+    t.D = sh->D;
+    t.ssb = sb;
+    t.ssd = sd;
+    t.sst = st;
+    t.dsb = db;
+    t.dsd = dd;
+    t.dstt = dt;
+    t.src_t_fast = t_fast(sd, st);
+    t.dst_t_fast = t_fast(dd, dt);
+    // 16-byte path: unit stride along each side's fast dimension, the other
+    // strides multiples of 4 elements, 16-byte aligned bases (4-byte
+    // elements only; the launcher ignores it for 2-byte ones)
+    const auto side_ok = [](const void *p, int64_t sb, int64_t sd, int64_t st, int32_t tf) {
+        const int64_t unit = tf ? st : sd, other = tf ? sd : st;
+        return unit == 1 && other % 4 == 0 && sb % 4 == 0 && aligned16(p);
+    };
+    t.vec = side_ok(src, sb, sd, st, t.src_t_fast) && side_ok(dst, db, dd, dt, t.dst_t_fast);
+    return t;
+}
+
+pararnn_status_t solve_common(pararnn_cell_t cell, const pararnn_shape_t *sh, const void *const *u,
+                              pararnn_dtype_t dt, const float *a, const float *const *s0,
+                              float *const *s, const pararnn_newton_t *opt, pararnn_info_t *info,
+                              void *ws, size_t ws_bytes, void *stream)
+{
+    pararnn_status_t st = check_newton(opt);
+    if (st != PARARNN_OK) return st;
+    Plan pl;
+    st = make_plan(cell, sh, opt, 0, pl);
+    if (st != PARARNN_OK) return st;
+    if (dt != PARARNN_F32 && dt != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;
+    const int G = cell_G(cell), S = cell_S(cell);
+    const size_t esize = dt == PARARNN_BF16 ? 2 : 4;
+    const Stage sg = stage_layout(cell, sh, esize, solve_ws_layout(cell, pl, opt).total);
+    const bool staged = sg.total > 0 && ws && ws_bytes >= sg.total && aligned16(ws) && u && s;
+    if (!staged) return solve_core(cell, sh, u, dt, a, s0, s, opt, info, ws, ws_bytes, stream);
+    for (int g = 0; g < G && sg.u; ++g)
+        if (!u[g]) return PARARNN_ERR_INVALID;
+    for (int c = 0; c < S; ++c)
+        if (!s[c]) return PARARNN_ERR_INVALID;
+
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    const int64_t dT = sh->T, dDT = sh->D * sh->T;  // dense channel-major strides
+    pararnn_shape_t sh2 = *sh;
+    const void *u2[4] = {nullptr, nullptr, nullptr, nullptr};
+    float *s2[2] = {nullptr, nullptr};
+    for (int g = 0; g < G; ++g) {
+        u2[g] = u[g];
+        if (!sg.u) continue;
+        u2[g] = base + sg.u_off + (size_t)g * sg.u_plane;
+        const TransArgs t = plane_copy(u[g], sh, sh->u_stride_b, sh->u_stride_d, sh->u_stride_t,
+                                       const_cast<void *>(u2[g]), dDT, dT, 1);
+        if (launch_transpose((int)esize, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    if (sg.u) {
+        sh2.u_stride_b = dDT;
+        sh2.u_stride_d = dT;
+        sh2.u_stride_t = 1;
+    }
+    for (int c = 0; c < S; ++c) {
+        s2[c] = s[c];
+        if (!sg.s) continue;
+        s2[c] = reinterpret_cast<float *>(base + sg.s_off + (size_t)c * sg.s_plane);
+        if (opt->init_from_output) {
+            const TransArgs t = plane_copy(s[c], sh, sh->s_stride_b, sh->s_stride_d,
+                                           sh->s_stride_t, s2[c], dDT, dT, 1);
+            if (launch_transpose(4, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+        }
+    }
+    if (sg.s) {
+        sh2.s_stride_b = dDT;
+        sh2.s_stride_d = dT;
+        sh2.s_stride_t = 1;
+    }
+    st = solve_core(cell, &sh2, u2, dt, a, s0, s2, opt, info, ws, ws_bytes, stream);
+    if (st != PARARNN_OK) return st;
+    for (int c = 0; c < S && sg.s; ++c) {
+        const TransArgs t = plane_copy(s2[c], sh, dDT, dT, 1, s[c], sh->s_stride_b,
+                                       sh->s_stride_d, sh->s_stride_t);
+        if (launch_transpose(4, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    return PARARNN_OK;
 }
 
 // ------------------------------------------------------------- adjoint ---
@@ -507,7 +652,11 @@ size_t pararnn_workspace_bytes(pararnn_cell_t cell, const pararnn_shape_t *shape
     if (make_plan(cell, shape, opt, adjoint ? 1 : 0, pl) != PARARNN_OK) return 0;
     if (adjoint) return adj_ws_layout(cell, pl).total;
     if (opt && (opt->max_iters < 0 || opt->max_iters > kMaxIters)) return 0;
-    return solve_ws_layout(cell, pl, opt).total;
+    // staging room for planes that are not time-contiguous (projections
+    // counted at 4 bytes, enough for either dtype)
+    const size_t base = solve_ws_layout(cell, pl, opt).total;
+    const Stage sg = stage_layout(cell, shape, 4, base);
+    return sg.total > 0 ? sg.total : base;
 }
 
 pararnn_status_t pararnn_solve_gru(const pararnn_shape_t *shape, const void *const u[3],

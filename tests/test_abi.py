@@ -86,6 +86,23 @@ def test_workspace_sizes():
     assert pr.workspace_bytes(7, pr.make_shape(1, 1, 1), n) == 0
 
 
+def test_workspace_includes_staging_for_time_major_planes():
+    """Planes that are not time-contiguous get room to be staged channel-major
+    (projections at 4 bytes per element, states at 4); channel-major planes
+    need none."""
+    n = pr.make_newton(1e-6, 20)
+    B, T, D = 8, 4096, 1024
+    N = B * T * D
+    dense = pr.workspace_bytes("gru", pr.make_shape(B, T, D), n)
+    tm_u = pr.workspace_bytes("gru", pr.make_shape(B, T, D, (T * 3 * D, 1, 3 * D)), n)
+    tm_both = pr.workspace_bytes("lstm", pr.make_shape(B, T, D, (T * 4 * D, 1, 4 * D),
+                                                       (T * D, 1, D)), n)
+    assert dense == 0
+    assert 3 * N * 4 <= tm_u < 3 * N * 4 + 4096
+    assert 4 * N * 4 + 2 * N * 4 <= tm_both < 6 * N * 4 + 4096
+    assert pr.workspace_bytes("gru", pr.make_shape(B, 1, D, (3 * D, 1, 3 * D)), n) == 0
+
+
 def test_scan_keeps_channels_in_one_workgroup_up_to_8192_steps():
     """The standalone scan's default tiling: no time blocks (workspace 0) up
     to 8192 steps, then 8192-step blocks with records and flags."""

@@ -71,6 +71,25 @@ def test_solve_time_major(cell, udt, T, KW):
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("KW", [(0, 0), (1, 2)])
+def test_time_major_gather_route(cell, KW):
+    """With a workspace too small to stage the planes channel-major, the solve
+    gathers the time-major steps directly; same bits either way."""
+    inp = make_inputs(cell, 2, 1000, 5, 4050, s0_std=0.1, f_bias=1.0)
+    u, a, s0 = dev_inputs(inp)
+    kw = dict(tol=1e-6, max_iters=40, steps_per_lane=KW[0], waves_per_block=KW[1])
+    ref, ref_info = solve(cell, u, a, s0, **kw)
+    _, ut = interleaved(u)
+    nws = pr.workspace_bytes(cell, pr.make_shape(2, 1000, 5),
+                             pr.make_newton(1e-6, 40, KW[0], KW[1]))
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+    got, info = solve(cell, ut, a, s0, workspace=ws, **kw)
+    for g, r in zip(got, ref):
+        assert torch.equal(g, r)
+    assert info == ref_info
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
 def test_solve_mixed_layouts(cell):
     """Time-major projections into channel-major states and the reverse."""
     inp = make_inputs(cell, 3, 777, 4, 4101, s0_std=0.2, f_bias=1.0)
