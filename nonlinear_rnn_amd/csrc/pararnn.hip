@@ -297,6 +297,47 @@ Stage stage_layout(pararnn_cell_t cell, const pararnn_shape_t *sh, size_t u_esiz
     return g;
 }
 
+// Staging room of the adjoint for planes that are not time-contiguous:
+// u-family (u in, du out) and s-family (s and dL/ds in, lambda out).
+struct AdjStage {
+    bool u = false, s = false;
+    size_t u_off = 0, u_plane = 0, du_off = 0, f_plane = 0, s_off = 0, gs_off = 0, lam_off = 0,
+           total = 0;
+};
+
+AdjStage adj_stage_layout(pararnn_cell_t cell, const pararnn_shape_t *sh, size_t u_esize,
+                          size_t base)
+{
+    AdjStage g;
+    if (!sh || sh->B <= 0 || sh->D <= 0 || sh->T <= 1) return g;
+    const int64_t n = sh->B * sh->D;
+    if (n > (int64_t(1) << 40) / sh->T) return g;
+    const int64_t e = n * sh->T;
+    g.u = sh->u_stride_t != 1;
+    g.s = sh->s_stride_t != 1;
+    if (!g.u && !g.s) return g;
+    const size_t G = cell_G(cell), S = cell_S(cell);
+    g.f_plane = align_up((size_t)e * sizeof(float));
+    size_t off = align_up(base);
+    if (g.u) {
+        g.u_plane = align_up((size_t)e * u_esize);
+        g.u_off = off;
+        off += G * g.u_plane;
+        g.du_off = off;
+        off += G * g.f_plane;
+    }
+    if (g.s) {
+        g.s_off = off;
+        off += S * g.f_plane;
+        g.gs_off = off;
+        off += S * g.f_plane;
+        g.lam_off = off;
+        off += S * g.f_plane;
+    }
+    g.total = off;
+    return g;
+}
+
 // Whether a plane with strides (sd, st) is walked faster along t than d.
 int32_t t_fast(int64_t sd, int64_t st) { return st == 1 ? 1 : sd == 1 ? 0 : (st <= sd ? 1 : 0); }
 
@@ -650,7 +691,11 @@ size_t pararnn_workspace_bytes(pararnn_cell_t cell, const pararnn_shape_t *shape
     if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return 0;
     Plan pl;
     if (make_plan(cell, shape, opt, adjoint ? 1 : 0, pl) != PARARNN_OK) return 0;
-    if (adjoint) return adj_ws_layout(cell, pl).total;
+    if (adjoint) {
+        const size_t base = adj_ws_layout(cell, pl).total;
+        const AdjStage sg = adj_stage_layout(cell, shape, 4, base);
+        return sg.total > 0 ? sg.total : base;
+    }
     if (opt && (opt->max_iters < 0 || opt->max_iters > kMaxIters)) return 0;
     // staging room for planes that are not time-contiguous (projections
     // counted at 4 bytes, enough for either dtype)
@@ -680,12 +725,105 @@ pararnn_status_t pararnn_solve_lstm(const pararnn_shape_t *shape, const void *co
     return solve_common(PARARNN_LSTM, shape, u, u_dtype, a, s0, s, opt, info, ws, ws_bytes, stream);
 }
 
+pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                              const void *const *u, pararnn_dtype_t u_dtype, const float *a,
+                              const float *const *s0, const float *const *s,
+                              const float *const *gs, float *const *du, float *da,
+                              float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
+                              void *ws, size_t ws_bytes, void *stream);
+
 pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *shape,
                                  const void *const *u, pararnn_dtype_t u_dtype, const float *a,
                                  const float *const *s0, const float *const *s,
                                  const float *const *gs, float *const *du, float *da,
                                  float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
                                  void *ws, size_t ws_bytes, void *stream)
+{
+    if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return PARARNN_ERR_INVALID;
+    if (u_dtype != PARARNN_F32 && u_dtype != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;
+    Plan pl;
+    pararnn_status_t st = make_plan(cell, shape, opt, 1, pl);
+    if (st != PARARNN_OK) return st;
+    const int G = cell_G(cell), S = cell_S(cell);
+    const size_t esize = u_dtype == PARARNN_BF16 ? 2 : 4;
+    const AdjStage sg = adj_stage_layout(cell, shape, esize, adj_ws_layout(cell, pl).total);
+    bool staged = sg.total > 0 && ws && ws_bytes >= sg.total && aligned16(ws) && u && s && gs &&
+                  du;
+    for (int g = 0; g < G && staged; ++g) staged = u[g] && du[g];
+    for (int c = 0; c < S && staged; ++c) staged = s[c] && (!lam || lam[c]);
+    if (!staged)
+        return adjoint_core(cell, shape, u, u_dtype, a, s0, s, gs, du, da, ds0, lam, opt, ws,
+                            ws_bytes, stream);
+
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    const int64_t dT = shape->T, dDT = shape->D * shape->T;
+    pararnn_shape_t sh2 = *shape;
+    const void *u2[4] = {};
+    float *du2[4] = {};
+    const float *s2[2] = {}, *gs2[2] = {};
+    float *lam2[2] = {};
+    for (int g = 0; g < G; ++g) {
+        u2[g] = u[g];
+        du2[g] = du[g];
+        if (!sg.u) continue;
+        u2[g] = base + sg.u_off + (size_t)g * sg.u_plane;
+        du2[g] = reinterpret_cast<float *>(base + sg.du_off + (size_t)g * sg.f_plane);
+        const TransArgs t = plane_copy(u[g], shape, shape->u_stride_b, shape->u_stride_d,
+                                       shape->u_stride_t, const_cast<void *>(u2[g]), dDT, dT, 1);
+        if (launch_transpose((int)esize, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    if (sg.u) {
+        sh2.u_stride_b = dDT;
+        sh2.u_stride_d = dT;
+        sh2.u_stride_t = 1;
+    }
+    for (int c = 0; c < S; ++c) {
+        s2[c] = s[c];
+        gs2[c] = gs[c];
+        lam2[c] = lam ? lam[c] : nullptr;
+        if (!sg.s) continue;
+        float *sp = reinterpret_cast<float *>(base + sg.s_off + (size_t)c * sg.f_plane);
+        TransArgs t = plane_copy(s[c], shape, shape->s_stride_b, shape->s_stride_d,
+                                 shape->s_stride_t, sp, dDT, dT, 1);
+        if (launch_transpose(4, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+        s2[c] = sp;
+        if (gs[c]) {
+            float *gp = reinterpret_cast<float *>(base + sg.gs_off + (size_t)c * sg.f_plane);
+            t = plane_copy(gs[c], shape, shape->s_stride_b, shape->s_stride_d, shape->s_stride_t,
+                           gp, dDT, dT, 1);
+            if (launch_transpose(4, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+            gs2[c] = gp;
+        }
+        if (lam) lam2[c] = reinterpret_cast<float *>(base + sg.lam_off + (size_t)c * sg.f_plane);
+    }
+    if (sg.s) {
+        sh2.s_stride_b = dDT;
+        sh2.s_stride_d = dT;
+        sh2.s_stride_t = 1;
+    }
+    st = adjoint_core(cell, &sh2, u2, u_dtype, a, s0, s2, gs2, du2, da, ds0, lam ? lam2 : nullptr,
+                      opt, ws, ws_bytes, stream);
+    if (st != PARARNN_OK) return st;
+    for (int g = 0; g < G && sg.u; ++g) {
+        const TransArgs t = plane_copy(du2[g], shape, dDT, dT, 1, du[g], shape->u_stride_b,
+                                       shape->u_stride_d, shape->u_stride_t);
+        if (launch_transpose(4, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    for (int c = 0; c < S && sg.s && lam; ++c) {
+        const TransArgs t = plane_copy(lam2[c], shape, dDT, dT, 1, lam[c], shape->s_stride_b,
+                                       shape->s_stride_d, shape->s_stride_t);
+        if (launch_transpose(4, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    return PARARNN_OK;
+}
+
+pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                              const void *const *u, pararnn_dtype_t u_dtype, const float *a,
+                              const float *const *s0, const float *const *s,
+                              const float *const *gs, float *const *du, float *da,
+                              float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
+                              void *ws, size_t ws_bytes, void *stream)
 {
     if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return PARARNN_ERR_INVALID;
     if (u_dtype != PARARNN_F32 && u_dtype != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;

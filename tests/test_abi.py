@@ -101,6 +101,11 @@ def test_workspace_includes_staging_for_time_major_planes():
     assert 3 * N * 4 <= tm_u < 3 * N * 4 + 4096
     assert 4 * N * 4 + 2 * N * 4 <= tm_both < 6 * N * 4 + 4096
     assert pr.workspace_bytes("gru", pr.make_shape(B, 1, D, (3 * D, 1, 3 * D)), n) == 0
+    # the adjoint stages u and dL/du (u-family), s, dL/ds and lambda (s-family)
+    adj_dense = pr.workspace_bytes("lstm", pr.make_shape(B, T, D), n, adjoint=True)
+    adj_tm = pr.workspace_bytes("lstm", pr.make_shape(B, T, D, (T * 4 * D, 1, 4 * D),
+                                                      (T * D, 1, D)), n, adjoint=True)
+    assert adj_dense + 14 * N * 4 <= adj_tm < adj_dense + 14 * N * 4 + 8192
 
 
 def test_scan_keeps_channels_in_one_workgroup_up_to_8192_steps():

@@ -157,6 +157,34 @@ def test_adjoint_time_major(cell, T, KW):
         assert np.abs(gd - r["du"][g]).max() <= 1e-5 * max(1.0, np.abs(r["du"][g]).max())
 
 
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+def test_adjoint_time_major_gather_route(cell):
+    """The adjoint with a base-size workspace gathers time-major steps
+    directly; bitwise the result of the staged route."""
+    inp = make_inputs(cell, 2, 900, 5, 4250, s0_std=0.3, f_bias=1.0, with_grad=True)
+    u, a, s0 = dev_inputs(inp)
+    h, _ = solve(cell, u, a, s0)
+    _, ut = interleaved(u)
+    st = [time_major(x) for x in h]
+    gs = [None] * (len(h) - 1) + [time_major(torch.from_numpy(inp.dh).to(DEV))]
+
+    def run(ws):
+        _, du = interleaved([torch.empty_like(x, dtype=torch.float32) for x in u])
+        out = dict(du=du, da=torch.empty((len(u), 5), device=DEV),
+                   ds0=[torch.empty_like(x) for x in s0], lam=[tm_empty(2, 5, 900) for _ in h])
+        return pr.adjoint(cell, ut, a, s0, st, gs, with_lambda=True, out=out, workspace=ws)
+
+    staged = run(None)
+    nws = pr.workspace_bytes(cell, pr.make_shape(2, 900, 5), pr.make_newton(0.0, 0),
+                             adjoint=True)
+    gathered = run(torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    for k in ("du", "ds0", "lam"):
+        for x, y in zip(staged[k], gathered[k]):
+            assert torch.equal(x, y), k
+    assert torch.equal(staged["da"], gathered["da"])
+
+
 @pytest.mark.parametrize("S", [1, 2])
 @pytest.mark.parametrize("reverse", [False, True])
 @pytest.mark.parametrize("T,KW", [(63, (1, 1)), (1000, (0, 0)), (5003, (1, 1))])
