@@ -368,6 +368,10 @@ def main():
     ap.add_argument("--layout", choices=["channel", "time"], default="channel",
                     help="channel: [B][D][T] planes (default); time: the gate blocks of one "
                          "[B][T][G*D] projection tensor and [B][T][D] states")
+    ap.add_argument("--route", choices=["staged", "gather"], default="staged",
+                    help="with --layout time: staged (planes copied channel-major through "
+                         "the workspace, the default) or gather (a channel-major-size "
+                         "workspace, every step loaded on its own)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB three "
                          "times (plain device copy used to calibrate HBM byte counters)")
@@ -417,13 +421,23 @@ def main():
         out = [torch.empty((w.B, w.T, D), dtype=torch.float32, device=dev).transpose(1, 2)
                for _ in range(w.S)]
     stream = torch.cuda.current_stream()
+    ws_solve = ws_adj = None
+    if time_major and args.route == "gather":
+        # workspaces of the channel-major size: no room to stage, so the
+        # kernels gather the time-major steps directly
+        dense = pr.make_shape(w.B, w.T, w.D)
+        nwt = pr.make_newton(w.tol, w.max_iters)
+        ws_solve = torch.empty(max(1, pr.workspace_bytes(w.cell, dense, nwt)),
+                               dtype=torch.uint8, device=dev)
+        ws_adj = torch.empty(max(1, pr.workspace_bytes(w.cell, dense, nwt, adjoint=True)),
+                             dtype=torch.uint8, device=dev)
 
     def solve(info):
         if w.cell == "gru":
             return pr.solve_gru(u, a, s0[0], out=out[0], tol=w.tol, max_iters=w.max_iters,
-                                info=info, stream=stream)[1]
+                                info=info, workspace=ws_solve, stream=stream)[1]
         return pr.solve_lstm(u, a, s0[0], s0[1], out=out, tol=w.tol, max_iters=w.max_iters,
-                             info=info, stream=stream)[1]
+                             info=info, workspace=ws_solve, stream=stream)[1]
 
     adj_out = None
     if w.adjoint:
@@ -440,7 +454,8 @@ def main():
 
     def backward():
         nonlocal adj_out
-        adj_out = pr.adjoint(w.cell, u, a, s0, out, gs, stream=stream, out=adj_out)
+        adj_out = pr.adjoint(w.cell, u, a, s0, out, gs, stream=stream, out=adj_out,
+                             workspace=ws_adj)
 
     # convergence report (untimed; the solve is deterministic)
     info = pr.read_info(solve(True))
@@ -493,7 +508,7 @@ def main():
     # the binding roof is the one the kernel runs closest to
     bound = "alu" if valu is not None and valu["frac"] > hbm["frac"] else "hbm"
     roof = valu if bound == "alu" else hbm
-    traffic = measured_traffic(args.workload + ("_time_major" if time_major else ""))
+    traffic = measured_traffic(args.workload + (f"_time_major_{args.route}" if time_major else ""))
     K, W, nb = pr.plan(w.cell, pr.make_shape(w.B, w.T, w.D))
     line = {
         "metric": METRIC,
@@ -510,7 +525,7 @@ def main():
         "data": data_recipe(w),
         "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol,
                    "layout": ("time-major: u gate blocks of one [B][T][G*D] tensor, "
-                              "states [B][T][D]") if time_major else
+                              f"states [B][T][D]; {args.route} route") if time_major else
                              "channel-major [B][D][T] planes",
                    "max_iters": w.max_iters, "seed": w.seed, "tiling": {"K": K, "W": W,
                    "time_blocks": nb}, "newton_updates": info["iters"],
