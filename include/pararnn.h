@@ -37,12 +37,13 @@
  *     a lane's steps are contiguous and load as 16-byte vectors.  Any other
  *     layout whose elements do not overlap is accepted, e.g. time-major
  *     [B][T][D] (stride_t = D, stride_d = 1, as a [B][T][G*D] projection
- *     gives per gate with stride_t = G*D).  The solves and the adjoint stage
- *     such planes channel-major in the workspace when it is at least
- *     pararnn_workspace_bytes(...) (which counts that room), run there and
- *     copy the results back; with a smaller workspace (the channel-major
- *     size) and in the scan and sequential calls, each step is gathered with
- *     its own 4-byte load instead.  Results are bitwise the same either way.
+ *     gives per gate with stride_t = G*D).  The solves, the adjoint and the
+ *     scan stage such planes channel-major in the workspace when it is at
+ *     least pararnn_workspace_bytes(...) / pararnn_scan_workspace_bytes(...)
+ *     (which count that room), run there and copy the results back; with a
+ *     smaller workspace (the channel-major size), and always in the
+ *     sequential call, each step is gathered with its own 4-byte load
+ *     instead.  Results are bitwise the same either way.
  *     pararnn_project writes channel-major planes directly.  Initial states are dense [B][D]; diagonal
  *     weights are dense [G][D] float32 in gate order (GRU: z, r, c;
  *     LSTM: i, f, g, o).  LSTM state order is (c, h).

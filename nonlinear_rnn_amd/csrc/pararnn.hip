@@ -502,18 +502,112 @@ pararnn_status_t make_scan_plan(int32_t S, const pararnn_shape_t *sh, const para
 
 extern "C" {
 
+// Staging room of the scan: S*S + S input planes (u strides) and S output
+// planes (s strides), when they are not time-contiguous.
+struct ScanStage {
+    bool in = false, out = false;
+    size_t in_off = 0, out_off = 0, plane = 0, total = 0;
+};
+
+ScanStage scan_stage_layout(int S, const pararnn_shape_t *sh, size_t base)
+{
+    ScanStage g;
+    if (!sh || sh->B <= 0 || sh->D <= 0 || sh->T <= 1) return g;
+    const int64_t n = sh->B * sh->D;
+    if (n > (int64_t(1) << 40) / sh->T) return g;
+    g.in = sh->u_stride_t != 1;
+    g.out = sh->s_stride_t != 1;
+    if (!g.in && !g.out) return g;
+    g.plane = align_up((size_t)(n * sh->T) * sizeof(float));
+    size_t off = align_up(base);
+    if (g.in) {
+        g.in_off = off;
+        off += (size_t)(S * S + S) * g.plane;
+    }
+    if (g.out) {
+        g.out_off = off;
+        off += (size_t)S * g.plane;
+    }
+    g.total = off;
+    return g;
+}
+
 size_t pararnn_scan_workspace_bytes(int32_t state_size, const pararnn_shape_t *shape,
                                     const pararnn_newton_t *opt)
 {
     Plan pl;
     if (make_scan_plan(state_size, shape, opt, pl) != PARARNN_OK) return 0;
-    return scan_ws_layout(state_size, pl).total;
+    const size_t base = scan_ws_layout(state_size, pl).total;
+    const ScanStage sg = scan_stage_layout(state_size, shape, base);
+    return sg.total > 0 ? sg.total : base;
 }
+
+pararnn_status_t scan_core(int32_t state_size, const pararnn_shape_t *shape,
+                           const float *const *Am, const float *const *bv, const float *const *x0,
+                           float *const *x, int32_t reverse, const pararnn_newton_t *opt, void *ws,
+                           size_t ws_bytes, void *stream);
 
 pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
                               const float *const *Am, const float *const *bv,
                               const float *const *x0, float *const *x, int32_t reverse,
                               const pararnn_newton_t *opt, void *ws, size_t ws_bytes, void *stream)
+{
+    Plan pl;
+    pararnn_status_t st = make_scan_plan(state_size, shape, opt, pl);
+    if (st != PARARNN_OK) return st;
+    const int S = state_size;
+    const ScanStage sg = scan_stage_layout(S, shape, scan_ws_layout(S, pl).total);
+    bool staged = sg.total > 0 && ws && ws_bytes >= sg.total && aligned16(ws) && Am && bv && x &&
+                  (reverse == 0 || reverse == 1);
+    for (int i = 0; i < S * S && staged; ++i) staged = Am[i] != nullptr;
+    for (int c = 0; c < S && staged; ++c) staged = bv[c] && x[c];
+    if (!staged) return scan_core(S, shape, Am, bv, x0, x, reverse, opt, ws, ws_bytes, stream);
+
+    hipStream_t strm = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    const int64_t dT = shape->T, dDT = shape->D * shape->T;
+    pararnn_shape_t sh2 = *shape;
+    const float *A2[4] = {}, *b2[2] = {};
+    float *x2[2] = {};
+    const auto stage_in = [&](const float *src, int k) -> const float * {
+        float *dst = reinterpret_cast<float *>(base + sg.in_off + (size_t)k * sg.plane);
+        const TransArgs t = plane_copy(src, shape, shape->u_stride_b, shape->u_stride_d,
+                                       shape->u_stride_t, dst, dDT, dT, 1);
+        return launch_transpose(4, t, strm) == hipSuccess ? dst : nullptr;
+    };
+    for (int i = 0; i < S * S; ++i) {
+        A2[i] = sg.in ? stage_in(Am[i], i) : Am[i];
+        if (!A2[i]) return PARARNN_ERR_HIP;
+    }
+    for (int c = 0; c < S; ++c) {
+        b2[c] = sg.in ? stage_in(bv[c], S * S + c) : bv[c];
+        if (!b2[c]) return PARARNN_ERR_HIP;
+        x2[c] = sg.out ? reinterpret_cast<float *>(base + sg.out_off + (size_t)c * sg.plane) : x[c];
+    }
+    if (sg.in) {
+        sh2.u_stride_b = dDT;
+        sh2.u_stride_d = dT;
+        sh2.u_stride_t = 1;
+    }
+    if (sg.out) {
+        sh2.s_stride_b = dDT;
+        sh2.s_stride_d = dT;
+        sh2.s_stride_t = 1;
+    }
+    st = scan_core(S, &sh2, A2, b2, x0, x2, reverse, opt, ws, ws_bytes, stream);
+    if (st != PARARNN_OK) return st;
+    for (int c = 0; c < S && sg.out; ++c) {
+        const TransArgs t = plane_copy(x2[c], shape, dDT, dT, 1, x[c], shape->s_stride_b,
+                                       shape->s_stride_d, shape->s_stride_t);
+        if (launch_transpose(4, t, strm) != hipSuccess) return PARARNN_ERR_HIP;
+    }
+    return PARARNN_OK;
+}
+
+pararnn_status_t scan_core(int32_t state_size, const pararnn_shape_t *shape,
+                           const float *const *Am, const float *const *bv, const float *const *x0,
+                           float *const *x, int32_t reverse, const pararnn_newton_t *opt, void *ws,
+                           size_t ws_bytes, void *stream)
 {
     Plan pl;
     pararnn_status_t st = make_scan_plan(state_size, shape, opt, pl);

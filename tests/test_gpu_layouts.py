@@ -8,6 +8,8 @@ and stores differ), and checks the time-major result against the CPU oracle
 at the usual tolerances (1e-5 max-abs for float32 states, 1e-5 * max(1,
 |ref|) for gradients and scans).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -204,6 +206,27 @@ def test_scan_time_major(S, reverse, T, KW):
     for g, r in zip(got, ref):
         assert g.stride()[1] == 1
         assert torch.equal(g, r)
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_scan_time_major_gather_route(S):
+    """The scan with a channel-major-size workspace gathers time-major steps;
+    bitwise the staged result."""
+    rng = np.random.default_rng(4350 + S)
+    T = 3000
+    A = rng.uniform(-0.7, 0.7, (S * S, 2, 3, T)).astype(np.float32)
+    b = rng.standard_normal((S, 2, 3, T)).astype(np.float32)
+    _, tm = interleaved([torch.from_numpy(x).to(DEV) for x in A] +
+                        [torch.from_numpy(x).to(DEV) for x in b])
+    kw = dict(steps_per_lane=1, waves_per_block=1)
+    staged = pr.scan(tm[:S * S], tm[S * S:], None, **kw)
+    nws = int(pr.load().pararnn_scan_workspace_bytes(
+        S, ctypes.byref(pr.make_shape(2, T, 3)), ctypes.byref(pr.make_newton(0.0, 0, 1, 1))))
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+    gathered = pr.scan(tm[:S * S], tm[S * S:], None, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    for x, y in zip(staged, gathered):
+        assert torch.equal(x, y)
 
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
