@@ -195,6 +195,8 @@ class Workspace:
     share one.  Each buffer is allocated on its own stream, so torch's
     allocator orders its reuse after that stream's work."""
 
+    MAX_STREAMS = 8  # buffers kept for the most recently used streams
+
     def __init__(self):
         self.buf = {}
 
@@ -203,11 +205,15 @@ class Workspace:
             return None
         s = stream if stream is not None else torch.cuda.current_stream(device)
         key = (torch.device(device).index, s.cuda_stream)
-        b = self.buf.get(key)
+        b = self.buf.pop(key, None)
         if b is None or b.numel() < nbytes:
             with torch.cuda.stream(s):
                 b = torch.empty(nbytes, dtype=torch.uint8, device=device)
-            self.buf[key] = b
+        self.buf[key] = b  # most recent last
+        while len(self.buf) > self.MAX_STREAMS:
+            # the oldest entry goes back to torch's allocator, which reuses it
+            # only in its own stream's order
+            self.buf.pop(next(iter(self.buf)))
         return b
 
 

@@ -240,3 +240,29 @@ def test_project_rejects_bad_arguments_before_any_device_call():
     assert call(good, x=None) == 1
     assert call(good, u=None) == 1
     assert call(pr.ProjShape(0, 8, 4, 6, 32, 4, 4, 48, 8), x=None, w=None, u=None) == 0
+
+
+def test_workspace_cache_is_per_stream_and_bounded(monkeypatch):
+    """Host logic of the binding's default workspace: one buffer per
+    (device, stream), reused while large enough, regrown when not, and only
+    the most recently used streams keep one."""
+    import contextlib
+
+    import torch
+    monkeypatch.setattr(torch.cuda, "stream", lambda s: contextlib.nullcontext())
+
+    class Stream:
+        def __init__(self, handle):
+            self.cuda_stream = handle
+
+    ws = pr.Workspace()
+    a = ws.get(64, "cpu", Stream(1))
+    assert ws.get(32, "cpu", Stream(1)) is a          # reused
+    assert ws.get(64, "cpu", Stream(2)) is not a      # another stream, another buffer
+    bigger = ws.get(128, "cpu", Stream(1))
+    assert bigger is not a and bigger.numel() == 128  # regrown
+    assert ws.get(0, "cpu", Stream(1)) is None
+    for h in range(100, 100 + 2 * pr.Workspace.MAX_STREAMS):
+        ws.get(16, "cpu", Stream(h))
+    assert len(ws.buf) == pr.Workspace.MAX_STREAMS
+    assert (None, 1) not in ws.buf                    # oldest streams dropped
