@@ -101,3 +101,41 @@ def test_projection_feeds_the_solve():
     ref = seq.gru_forward(u_dev, a.cpu().numpy(), h0.cpu().numpy())
     assert np.max(np.abs(h.cpu().numpy() - ref)) < 1e-5
     check(u, x64, w64, None, out_bf16=True)
+
+
+@pytest.mark.parametrize("key", ["gru_small", "gru_f32", "lstm_f32", "gru_bf16_long", "lstm_fwd_bwd"])
+def test_project_workload_scale(key):
+    """The projection of each workload at full size, in the launch the bench
+    times (x [B][T][I=D] bf16, W [G*D][I] bf16, output [B][G*D][T] in the
+    workload's projection dtype), checked against the oracle on every output
+    row at sampled time steps (all column tiles) and on every time step of
+    sampled rows (all row tiles), both including the tile edges."""
+    from nonlinear_rnn_amd.inputs import WORKLOADS
+    w = WORKLOADS[key]
+    I, M = w.D, (3 if w.cell == "gru" else 4) * w.D
+    gen = torch.Generator(device="cpu").manual_seed(w.seed + 200)
+    x = torch.randn((w.B, w.T, I), generator=gen).to(torch.bfloat16).to(DEV)
+    wt = (torch.randn((M, I), generator=gen) / I ** 0.5).to(torch.bfloat16)
+    bias = torch.randn(M, generator=gen)
+    w64, b64 = wt.to(torch.float64).numpy(), bias.to(torch.float64).numpy()
+    out_dtype = torch.bfloat16 if w.u_dtype == "bf16" else torch.float32
+    out = torch.empty((w.B, M, w.T), dtype=out_dtype, device=DEV)
+    pr.project(x, wt.to(DEV), bias.to(DEV), out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(w.seed + 200)
+
+    def edges(n):
+        ks = sorted({1, n // 512, n // 256} | set(rng.integers(1, n // 256 + 2, 4).tolist()))
+        e = {0, n - 1} | {v for k in ks for v in (256 * k - 1, 256 * k) if 0 < v < n}
+        return sorted(e | set(rng.integers(0, n, 16).tolist()))
+
+    ts = edges(w.T)
+    tsel = torch.tensor(ts, device=DEV)
+    xs64 = x[:, tsel].to(torch.float64).cpu().numpy()
+    check(out[:, :, tsel], xs64, w64, b64, out_bf16=out_dtype == torch.bfloat16)
+    ms = edges(M)
+    msel = torch.tensor(ms, device=DEV)
+    for b in sorted({0, w.B - 1}):
+        xb64 = x[b:b + 1].to(torch.float64).cpu().numpy()
+        check(out[b:b + 1, msel], xb64, w64[ms], b64[ms], out_bf16=out_dtype == torch.bfloat16)
