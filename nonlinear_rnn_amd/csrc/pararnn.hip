@@ -498,10 +498,6 @@ pararnn_status_t make_scan_plan(int32_t S, const pararnn_shape_t *sh, const para
     return make_plan(S == 2 ? PARARNN_LSTM : PARARNN_GRU, sh, opt, 2, pl);
 }
 
-}  // namespace
-
-extern "C" {
-
 // Staging room of the scan: S*S + S input planes (u strides) and S output
 // planes (s strides), when they are not time-contiguous.
 struct ScanStage {
@@ -532,6 +528,22 @@ ScanStage scan_stage_layout(int S, const pararnn_shape_t *sh, size_t base)
     return g;
 }
 
+pararnn_status_t scan_core(int32_t state_size, const pararnn_shape_t *shape,
+                           const float *const *Am, const float *const *bv, const float *const *x0,
+                           float *const *x, int32_t reverse, const pararnn_newton_t *opt, void *ws,
+                           size_t ws_bytes, void *stream);
+
+pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
+                              const void *const *u, pararnn_dtype_t u_dtype, const float *a,
+                              const float *const *s0, const float *const *s,
+                              const float *const *gs, float *const *du, float *da,
+                              float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
+                              void *ws, size_t ws_bytes, void *stream);
+
+}  // namespace
+
+extern "C" {
+
 size_t pararnn_scan_workspace_bytes(int32_t state_size, const pararnn_shape_t *shape,
                                     const pararnn_newton_t *opt)
 {
@@ -541,11 +553,6 @@ size_t pararnn_scan_workspace_bytes(int32_t state_size, const pararnn_shape_t *s
     const ScanStage sg = scan_stage_layout(state_size, shape, base);
     return sg.total > 0 ? sg.total : base;
 }
-
-pararnn_status_t scan_core(int32_t state_size, const pararnn_shape_t *shape,
-                           const float *const *Am, const float *const *bv, const float *const *x0,
-                           float *const *x, int32_t reverse, const pararnn_newton_t *opt, void *ws,
-                           size_t ws_bytes, void *stream);
 
 pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
                               const float *const *Am, const float *const *bv,
@@ -603,6 +610,10 @@ pararnn_status_t pararnn_scan(int32_t state_size, const pararnn_shape_t *shape,
     }
     return PARARNN_OK;
 }
+
+}  // extern "C"
+
+namespace {
 
 pararnn_status_t scan_core(int32_t state_size, const pararnn_shape_t *shape,
                            const float *const *Am, const float *const *bv, const float *const *x0,
@@ -667,6 +678,10 @@ pararnn_status_t scan_core(int32_t state_size, const pararnn_shape_t *shape,
     return launch_scan(S, pl.K, pl.W, reverse != 0, groups, strm, A) == hipSuccess ? PARARNN_OK
                                                                                   : PARARNN_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 pararnn_status_t pararnn_project(const pararnn_proj_shape_t *sh, const void *x, const void *w,
                                  const float *bias, void *u, pararnn_dtype_t u_dtype,
@@ -819,13 +834,6 @@ pararnn_status_t pararnn_solve_lstm(const pararnn_shape_t *shape, const void *co
     return solve_common(PARARNN_LSTM, shape, u, u_dtype, a, s0, s, opt, info, ws, ws_bytes, stream);
 }
 
-pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
-                              const void *const *u, pararnn_dtype_t u_dtype, const float *a,
-                              const float *const *s0, const float *const *s,
-                              const float *const *gs, float *const *du, float *da,
-                              float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
-                              void *ws, size_t ws_bytes, void *stream);
-
 pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *shape,
                                  const void *const *u, pararnn_dtype_t u_dtype, const float *a,
                                  const float *const *s0, const float *const *s,
@@ -911,6 +919,10 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
     }
     return PARARNN_OK;
 }
+
+}  // extern "C"
+
+namespace {
 
 pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
                               const void *const *u, pararnn_dtype_t u_dtype, const float *a,
@@ -1020,4 +1032,4 @@ pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
     return PARARNN_OK;
 }
 
-}  // extern "C"
+}  // namespace

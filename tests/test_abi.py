@@ -32,6 +32,22 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_library_exports_no_undeclared_c_functions():
+    """Every C-linkage function the library defines is one the header
+    declares: internal helpers stay out of the exported name space."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", pr.LIB_PATH], check=True,
+                         stdout=subprocess.PIPE, text=True).stdout
+    funcs = sorted({ln.split()[2] for ln in out.splitlines()
+                    if len(ln.split()) == 3 and ln.split()[1] == "T"
+                    and not ln.split()[2].startswith("_")})
+    assert funcs == _declared()
+
+
 def test_status_strings():
     assert pr.status_string(0) == "ok"
     for s in range(1, 5):
