@@ -98,7 +98,9 @@ typedef struct {
                                  the output planes; 0: from s = 0             */
 } pararnn_newton_t;
 
-/* Written on the device by the solve (pass a device pointer, or NULL). */
+/* Written on the device by the solve (pass a device pointer, or NULL): each
+ * work unit stores its own final max|r| and update count in the workspace,
+ * and a one-workgroup pass after the solve folds them into this record. */
 typedef struct {
     int32_t iters;        /* max Newton updates applied, over channels       */
     int32_t converged;    /* 1 iff every channel stopped with max|r| < tol    */
@@ -110,7 +112,12 @@ typedef struct {
 
 /* Bytes of device workspace pararnn_solve_* / pararnn_adjoint need for this
  * problem and tiling (0 is possible).  Returns 0 on a bad argument too; the
- * solve itself reports the error.  For the adjoint pass adjoint = 1. */
+ * solve itself reports the error.  For the adjoint pass adjoint = 1.
+ * For a solve the figure counts the time-block hand-off (several blocks per
+ * channel), 8 bytes per work unit for the convergence records an info
+ * record is folded from, and the staging room of planes that are not
+ * time-contiguous; a solve without an info record, on time-contiguous
+ * planes with one block per channel, runs with no workspace at all. */
 size_t pararnn_workspace_bytes(pararnn_cell_t cell, const pararnn_shape_t *shape,
                                const pararnn_newton_t *opt, int adjoint);
 

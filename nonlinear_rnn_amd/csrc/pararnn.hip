@@ -137,26 +137,38 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
     return PARARNN_OK;
 }
 
+// Solve workspace: the time-block hand-off of a multi-block solve (ticket,
+// flags, per-iteration block records, warm-start boundary states), then the
+// per-unit convergence records the info fold reads (needed only when an info
+// record is requested).
 struct SolveWs {
-    size_t ticket = 0, flags = 0, records = 0, hin0 = 0, total = 0;
+    size_t ticket = 0, flags = 0, records = 0, hin0 = 0;
+    size_t multi = 0;      // bytes of the hand-off part (0 with one block per channel)
+    size_t unit_info = 0;  // offset of the per-unit records, 8 bytes a unit
+    size_t total = 0;
 };
 
 SolveWs solve_ws_layout(pararnn_cell_t cell, const Plan &pl, const pararnn_newton_t *opt)
 {
     SolveWs w;
-    if (pl.nb <= 1) return w;
-    const int64_t cap = opt ? opt->max_iters : 0;
     size_t off = 0;
-    w.ticket = off;
-    off += kAlign;
-    w.flags = off;
-    off = align_up(off + (size_t)pl.units * sizeof(int32_t));
-    w.records = off;
-    off = align_up(off + (size_t)pl.units * (size_t)(cap + 1) * rec_floats(cell) * sizeof(float));
-    if (opt && opt->init_from_output) {
-        w.hin0 = off;
-        off = align_up(off + (size_t)pl.units * cell_S(cell) * sizeof(float));
+    if (pl.nb > 1) {
+        const int64_t cap = opt ? opt->max_iters : 0;
+        w.ticket = off;
+        off += kAlign;
+        w.flags = off;
+        off = align_up(off + (size_t)pl.units * sizeof(int32_t));
+        w.records = off;
+        off = align_up(off +
+                       (size_t)pl.units * (size_t)(cap + 1) * rec_floats(cell) * sizeof(float));
+        if (opt && opt->init_from_output) {
+            w.hin0 = off;
+            off = align_up(off + (size_t)pl.units * cell_S(cell) * sizeof(float));
+        }
+        w.multi = off;
     }
+    w.unit_info = off;
+    if (pl.units > 0) off = align_up(off + (size_t)pl.units * 2 * sizeof(uint32_t));
     w.total = off;
     return w;
 }
@@ -193,7 +205,8 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
             if (!s0[c] || !s[c]) return PARARNN_ERR_INVALID;
     }
     const SolveWs wl = solve_ws_layout(cell, pl, opt);
-    if (work && wl.total > 0 && (!ws || ws_bytes < wl.total || !aligned16(ws)))
+    const size_t need = info ? wl.total : wl.multi;
+    if (work && need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
         return PARARNN_ERR_WORKSPACE;
     hipStream_t strm = static_cast<hipStream_t>(stream);
 
@@ -220,7 +233,6 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
     A.cap = opt->max_iters;
     A.nb = (int32_t)pl.nb;
     A.init_from_output = opt->init_from_output;
-    A.info = info;
     const int ve = dt == PARARNN_BF16 ? 8 : 4;
     bool uv = sh->u_stride_t == 1 && (sh->T % ve == 0) && (sh->u_stride_b % ve == 0) &&
               (sh->u_stride_d % ve == 0);
@@ -230,24 +242,30 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
     for (int c = 0; c < S && work; ++c) sv = sv && aligned16(s[c]);
     A.u_vec = uv ? 1 : 0;
     A.s_vec = sv ? 1 : 0;
-    if (wl.total > 0) {
-        char *base = static_cast<char *>(ws);
+    char *base = static_cast<char *>(ws);
+    if (work && wl.multi > 0) {
         A.ticket = reinterpret_cast<uint32_t *>(base + wl.ticket);
         A.flags = reinterpret_cast<int32_t *>(base + wl.flags);
         A.records = reinterpret_cast<float *>(base + wl.records);
         A.hin0 = opt->init_from_output ? reinterpret_cast<float *>(base + wl.hin0) : nullptr;
     }
-    if (!work) A.nb = 1;
+    if (work && info) A.unit_info = reinterpret_cast<uint32_t *>(base + wl.unit_info);
+    uint32_t tolb;
+    std::memcpy(&tolb, &opt->tol, sizeof(tolb));
+    const auto fold_info = [&]() -> pararnn_status_t {
+        if (!info) return PARARNN_OK;
+        hipLaunchKernelGGL(info_fold_kernel, dim3(1), dim3(kFoldThreads), 0, strm,
+                           A.unit_info, work ? pl.units : (int64_t)0, tolb, info);
+        return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+    };
+    if (!work) return fold_info();
 
-    const bool need_init = info != nullptr || (work && pl.nb > 1);
-    if (need_init) {
-        const int64_t n = (work && pl.nb > 1) ? pl.units : 1;
+    if (pl.nb > 1) {
         const int tpb = 256;
-        hipLaunchKernelGGL(solve_init_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
-                           strm, A, S, work ? pl.units : 0, (int32_t)pl.P);
+        hipLaunchKernelGGL(solve_init_kernel, dim3((unsigned)((pl.units + tpb - 1) / tpb)),
+                           dim3(tpb), 0, strm, A, S, pl.units, (int32_t)pl.P);
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
     }
-    if (!work) return PARARNN_OK;
     const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
     const int variant = sh->T % pl.P != 0 ? kNewtonAny
                         : pl.nb == 1      ? kNewtonFullSingle
@@ -259,7 +277,8 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
     else
         e = dt == PARARNN_BF16 ? launch_newton_lstm_bf16(pl.K, pl.W, variant, groups, strm, A)
                                : launch_newton_lstm_f32(pl.K, pl.W, variant, groups, strm, A);
-    return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+    if (e != hipSuccess) return PARARNN_ERR_HIP;
+    return fold_info();
 }
 
 // ------------------------------------------------- time-major staging ---

@@ -69,7 +69,7 @@ struct SolveArgs {
     int32_t *flags;
     float *records;
     float *hin0;
-    pararnn_info_t *info;
+    uint32_t *unit_info;  // per work unit: (max|r| bits, updates), or null
 };
 
 template <class M>
@@ -494,15 +494,11 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         for (int kk = 0; kk < K; ++kk) tmp[kk] = vget(s[kk], c);
         store_steps<K>(A.s[c] + soff, t0, T, A.sst, A.s_vec != 0, tmp);
     }
-    if (A.info && threadIdx.x == 0) {
-        pararnn_info_t *inf = A.info;
-        atomicMax(&inf->iters, it);
-        if (!(bmx < tolb)) atomicAnd(&inf->converged, 0);
-        atomicMax(reinterpret_cast<unsigned int *>(&inf->max_abs_res), bmx);
-        if (bmx > 0x7f800000u) atomicOr(&inf->nan_seen, 1);
-        atomicAdd(reinterpret_cast<unsigned long long *>(&inf->iters_sum),
-                  (unsigned long long)it);
-    }
+    // The unit's own convergence record, folded into the info record by a
+    // separate pass: atomics on one shared record from every workgroup
+    // serialise on a single address and stall the whole solve.
+    if (A.unit_info && threadIdx.x == 0)
+        *reinterpret_cast<uint2 *>(A.unit_info + 2 * unit) = make_uint2(bmx, (uint32_t)it);
 }
 
 // One work unit per workgroup.  Serves every case: several time blocks per
@@ -578,22 +574,12 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit
-// Clears the per-launch state (ticket counter, block flags, info record) and
-// gathers the initial boundary states a warm-started multi-block solve needs.
+// Clears the per-launch state of a multi-block solve (ticket counter, block
+// flags) and gathers the initial boundary states a warm start needs.
 __global__ void solve_init_kernel(SolveArgs A, int32_t S, int64_t units, int32_t P)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) {
-        if (A.ticket) *A.ticket = 0u;
-        if (A.info) {
-            A.info->iters = 0;
-            A.info->converged = 1;
-            A.info->max_abs_res = 0.0f;
-            A.info->nan_seen = 0;
-            A.info->iters_sum = 0;
-            A.info->units = units;
-        }
-    }
+    if (i == 0 && A.ticket) *A.ticket = 0u;
     if (i < units && A.flags) {
         A.flags[i] = 0;
         if (A.init_from_output && A.hin0) {
@@ -604,6 +590,54 @@ __global__ void solve_init_kernel(SolveArgs A, int32_t S, int64_t units, int32_t
                 A.hin0[i * S + c] =
                     k > 0 ? A.s[c][b * A.ssb + d * A.ssd + ((int64_t)k * P - 1) * A.sst] : 0.0f;
         }
+    }
+}
+
+// The info record from the units' own records: max updates, max of the
+// final max|r| (bit patterns of non-negative floats order like the floats,
+// NaN above +inf), converged iff that maximum is below tol, and the sum of
+// updates.  Every field is an exact integer or max fold, so the result does
+// not depend on the order.  One workgroup; the records are 8 bytes a unit.
+constexpr int kFoldThreads = 1024;
+__global__ void __launch_bounds__(kFoldThreads)
+    info_fold_kernel(const uint32_t *rec, int64_t units, uint32_t tolb, pararnn_info_t *info)
+{
+    uint32_t mx = 0u, itmax = 0u;
+    unsigned long long sum = 0ull;
+    const uint2 *r2 = reinterpret_cast<const uint2 *>(rec);
+    for (int64_t i = threadIdx.x; i < units; i += kFoldThreads) {
+        const uint2 r = r2[i];
+        mx = max(mx, r.x);
+        itmax = max(itmax, r.y);
+        sum += r.y;
+    }
+    __shared__ uint32_t smx[kFoldThreads / kWave], sit[kFoldThreads / kWave];
+    __shared__ unsigned long long ssum[kFoldThreads / kWave];
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+        itmax = max(itmax, (uint32_t)__shfl_xor((int)itmax, o));
+        sum += (unsigned long long)__shfl_xor((long long)sum, o);
+    }
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        smx[wave] = mx;
+        sit[wave] = itmax;
+        ssum[wave] = sum;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kFoldThreads / kWave; ++w) {
+            mx = max(mx, smx[w]);
+            itmax = max(itmax, sit[w]);
+            sum += ssum[w];
+        }
+        info->iters = (int32_t)itmax;
+        info->converged = (units == 0 || mx < tolb) ? 1 : 0;
+        info->max_abs_res = __uint_as_float(mx);
+        info->nan_seen = mx > 0x7f800000u ? 1 : 0;
+        info->iters_sum = (int64_t)sum;
+        info->units = units;
     }
 }
 

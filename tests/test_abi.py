@@ -88,7 +88,8 @@ def test_wide_lane_tiling_is_gru_forward_only():
 
 def test_workspace_sizes():
     n = pr.make_newton(1e-6, 20)
-    assert pr.workspace_bytes("gru", pr.make_shape(8, 4096, 1024), n) == 0
+    # one block per channel: only the per-unit convergence records
+    assert pr.workspace_bytes("gru", pr.make_shape(8, 4096, 1024), n) == 8192 * 8
     ws = pr.workspace_bytes("gru", pr.make_shape(4, 16384, 4096), n)
     units = 4 * 4096 * 2  # two 8192-step blocks per channel
     assert ws >= units * 4 + units * 21 * 4 * 4
@@ -113,10 +114,10 @@ def test_workspace_includes_staging_for_time_major_planes():
     tm_u = pr.workspace_bytes("gru", pr.make_shape(B, T, D, (T * 3 * D, 1, 3 * D)), n)
     tm_both = pr.workspace_bytes("lstm", pr.make_shape(B, T, D, (T * 4 * D, 1, 4 * D),
                                                        (T * D, 1, D)), n)
-    assert dense == 0
-    assert 3 * N * 4 <= tm_u < 3 * N * 4 + 4096
-    assert 4 * N * 4 + 2 * N * 4 <= tm_both < 6 * N * 4 + 4096
-    assert pr.workspace_bytes("gru", pr.make_shape(B, 1, D, (3 * D, 1, 3 * D)), n) == 0
+    assert dense == B * D * 8  # the per-unit convergence records only
+    assert dense + 3 * N * 4 <= tm_u < dense + 3 * N * 4 + 4096
+    assert dense + 4 * N * 4 + 2 * N * 4 <= tm_both < dense + 6 * N * 4 + 4096
+    assert pr.workspace_bytes("gru", pr.make_shape(B, 1, D, (3 * D, 1, 3 * D)), n) == B * D * 8
     # the adjoint stages u and dL/du (u-family), s, dL/ds and lambda (s-family)
     adj_dense = pr.workspace_bytes("lstm", pr.make_shape(B, T, D), n, adjoint=True)
     adj_tm = pr.workspace_bytes("lstm", pr.make_shape(B, T, D, (T * 4 * D, 1, 4 * D),
@@ -167,11 +168,11 @@ def test_plane_layouts_accepted_and_rejected():
     assert not ok((2 ** 62 + 16, 2 ** 61, 1))    # offsets past int64
 
 
-def _call_gru(shape, newton, u=(1, 1, 1), a=1, h0=1, h=1, ws=None, nws=0):
+def _call_gru(shape, newton, u=(1, 1, 1), a=1, h0=1, h=1, ws=None, nws=0, info=None):
     lib = pr.load()
     arr = (ctypes.c_void_p * 3)(*[x or None for x in u])
     return lib.pararnn_solve_gru(ctypes.byref(shape) if shape is not None else None, arr, 0,
-                                 a, h0, h, ctypes.byref(newton) if newton else None, None,
+                                 a, h0, h, ctypes.byref(newton) if newton else None, info,
                                  ws, nws, None)
 
 
@@ -196,8 +197,15 @@ def test_solve_rejects_bad_arguments_before_any_device_call():
     big = pr.make_shape(2, 200, 3)
     assert _call_gru(big, nb) == 3
     need = pr.workspace_bytes("gru", big, nb)
-    assert _call_gru(big, nb, ws=16, nws=need - 1) == 3
+    assert _call_gru(big, nb, ws=16, nws=need - 1, info=16) == 3
+    units_big = 2 * 3 * 4
+    assert _call_gru(big, nb, ws=16, nws=need - 256 * ((units_big * 8 + 255) // 256) - 1) == 3
     assert _call_gru(big, nb, ws=8, nws=need) == 3                     # misaligned
+    # an info record is folded from per-unit records kept in the workspace
+    units = 2 * 3
+    assert pr.workspace_bytes("gru", good, n) == 256 * ((units * 8 + 255) // 256)
+    assert _call_gru(good, n, info=16) == 3
+    assert _call_gru(good, n, info=16, ws=16, nws=units * 8 - 1) == 3
 
 
 def test_lstm_and_adjoint_reject_bad_arguments():
