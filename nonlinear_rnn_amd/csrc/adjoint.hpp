@@ -182,10 +182,8 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
     int64_t ch;
     int32_t k;
     if (A.nb > 1) {
-        if (threadIdx.x == 0) s_ticket = (int64_t)atomicAdd(A.ticket, 1u);
-        __syncthreads();
         int32_t q;
-        ticket_to_unit(s_ticket, A.nb, ch, q);
+        take_unit(A.ticket, A.channels, A.nb, s_ticket, ch, q);
         k = A.nb - 1 - q;  // later time blocks take earlier tickets
     } else {
         ch = xcd_channel(blockIdx.x, A.channels);

@@ -89,9 +89,7 @@ __global__ void __launch_bounds__(W * kWave) scan_kernel(ScanArgs A)
     int64_t ch;
     int32_t r;  // rank of this time block in scan order
     if (A.nb > 1) {
-        if (threadIdx.x == 0) s_ticket = (int64_t)atomicAdd(A.ticket, 1u);
-        __syncthreads();
-        ticket_to_unit(s_ticket, A.nb, ch, r);
+        take_unit(A.ticket, A.channels, A.nb, s_ticket, ch, r);
     } else {
         ch = xcd_channel(blockIdx.x, A.channels);
         r = 0;

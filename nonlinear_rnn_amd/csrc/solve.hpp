@@ -215,17 +215,31 @@ __device__ __forceinline__ void vset(Vec2 &v, int i, float x)
         v.x0 = x;
 }
 
-// Maps (channel, time block) to a dynamic ticket so that block k-1 of a
-// channel always holds a smaller ticket than block k (it started earlier and
-// is resident or done: the waits below cannot deadlock).  Tickets 8 apart
-// belong to one channel, so when workgroups are spread round-robin over the
-// 8 XCDs the blocks of a channel tend to share an XCD and its L2.
-__device__ __forceinline__ void ticket_to_unit(int64_t t, int32_t nb, int64_t &ch, int32_t &k)
+// Dynamic work units of a multi-block launch (grid 8 * ceil(channels / 8) *
+// nb, the channels past the last one are padding).  A workgroup takes the
+// next ticket of one counter once it is resident.  Tickets run over groups
+// of kTicketGroup channels, handing out time-block rank 0 of every channel
+// in the group, then rank 1, and so on, so a channel's rank r-1 always
+// holds a smaller ticket than its rank r: it is resident or done whenever
+// rank r runs, and the waits on predecessors cannot deadlock.  Spacing a
+// channel's blocks a group apart lets a predecessor run ahead of its
+// successor instead of both spinning in step (adjacent tickets measured up
+// to 29% slower on the adjoint, 7-11% on the solve and the scan).
+constexpr int64_t kTicketGroup = 1024;
+
+__device__ __forceinline__ void take_unit(uint32_t *ticket, int64_t channels, int32_t nb,
+                                          int64_t &s_ticket, int64_t &ch, int32_t &r)
 {
-    const int64_t grp = 8 * (int64_t)nb;
-    const int64_t g = t / grp, r = t - g * grp;
-    k = (int32_t)(r >> 3);
-    ch = g * 8 + (r & 7);
+    if (threadIdx.x == 0) s_ticket = (int64_t)atomicAdd(ticket, 1u);
+    __syncthreads();
+    const int64_t t = s_ticket;
+    const int64_t padded = (channels + 7) / 8 * 8;
+    const int64_t g = t / (kTicketGroup * nb);
+    const int64_t base = g * kTicketGroup;
+    const int64_t size = padded - base < kTicketGroup ? padded - base : kTicketGroup;
+    const int64_t within = t - base * nb;
+    r = (int32_t)(within / size);
+    ch = base + (within - (int64_t)r * size);
 }
 
 // Map held by lane `src` of the wave, read by every lane (wave-uniform).
@@ -521,9 +535,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
     int64_t ch;
     int32_t k;
     if (!SINGLE && A.nb > 1) {
-        if (threadIdx.x == 0) s_ticket = (int64_t)atomicAdd(A.ticket, 1u);
-        __syncthreads();
-        ticket_to_unit(s_ticket, A.nb, ch, k);
+        take_unit(A.ticket, A.channels, A.nb, s_ticket, ch, k);
     } else {
         ch = xcd_channel(blockIdx.x, A.channels);
         k = 0;
