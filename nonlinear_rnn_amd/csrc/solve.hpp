@@ -292,28 +292,33 @@ __device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_
         }
     }
     after_flag();
-    // Pass 2: blocks start..p-1 all report |r| < tol at `it`, so they stop
-    // now (their carry-out is zero); the carry is the ordered fold of p..k-1.
+    // Pass 2: the first block p in start..k-1 that does not report |r| < tol
+    // at `it`; blocks start..p-1 stop now (their carry-out is zero) and the
+    // carry is the ordered fold of p..k-1.  Each lane loads its block's whole
+    // record (bit and map) at once, so finding p and folding from it take
+    // one round trip per window of 64 blocks, not two.
     int32_t p = k;
+    din = vzero<V>();
     for (int32_t lo = start; lo < k; lo += kWave) {
         const int32_t j = lo + lane;
         const bool mine = j < k;
-        const uint32_t cb = mine ? rec_cbit(rec + j * rstride + it * RF, RF) : 1u;
-        const unsigned long long open = __ballot(mine && cb == 0u);
-        if (open) {
-            p = lo + __ffsll((long long)open) - 1;
-            break;
+        M mj = identity_map(M{});
+        uint32_t cb = 1u;
+        if (mine) {
+            rec_load(rec + j * rstride + it * RF, mj);
+            cb = rec_cbit(rec + j * rstride + it * RF, RF);
         }
+        int32_t q0 = 0;
+        if (p == k) {
+            const unsigned long long open = __ballot(mine && cb == 0u);
+            if (!open) continue;
+            q0 = __ffsll((long long)open) - 1;
+            p = lo + q0;
+        }
+        const int32_t n = (k - lo) < kWave ? (k - lo) : kWave;
+        for (int32_t q = q0; q < n; ++q) din = apply(readlane_map(mj, q), din);
     }
     pred_stopped = (p == k);
-    din = vzero<V>();
-    for (int32_t lo = p; lo < k; lo += kWave) {
-        const int32_t j = lo + lane;
-        M mj = identity_map(M{});
-        if (j < k) rec_load(rec + j * rstride + it * RF, mj);
-        const int32_t n = (k - lo) < kWave ? (k - lo) : kWave;
-        for (int32_t q = 0; q < n; ++q) din = apply(readlane_map(mj, q), din);
-    }
 }
 
 template <class M>
@@ -392,12 +397,19 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     // Newton converges quadratically: once max|r| < sqrt(tol) (A.guess_tol)
     // the next residual is expected below tol, so that evaluation skips the
     // Jacobian and the scan.  A wrong guess only costs a second evaluation of
-    // the same iterate.  (Whole channels only: a time block must publish its
-    // map.)
-    const uint32_t predb = multi ? 0u : __float_as_uint(A.guess_tol);
+    // the same iterate.  A time block whose residual passes must still learn
+    // whether its predecessors stop at this iteration: it looks back first
+    // and stops (publishing only its stop flag) if they do; otherwise it
+    // evaluates the iterate in full, publishes its map and reuses the carry
+    // it already has.  The stopping iteration of every unit is the one the
+    // full evaluation would give.
+    const uint32_t predb = __float_as_uint(A.guess_tol);
     M m[MAPS_LDS ? 1 : K];  // running composition of the lane's steps 0..kk
     int32_t it = 0;
     uint32_t bmx = 0;
+    bool carry_known = false;  // the probe of this iteration already looked back
+    V din_probe = vzero<V>();
+    bool stopped_probe = true;
     bool ronly = false;  // this evaluation is the predicted last one
     int xp = 0;          // LDS exchange slot parity (alternates every exchange)
     for (;; ++it) {
@@ -422,7 +434,16 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 #pragma unroll
             for (int j = 1; j < W; ++j) bmx = max(bmx, sm.slots[xp][j].mx);
             xp ^= 1;
-            if (bmx < tolb || it == A.cap) break;
+            if (it == A.cap) break;
+            if (bmx < tolb) {
+                if (!multi) break;
+                if (k > 0) look_back<M, V>(A, ch, k, it, din_probe, stopped_probe);
+                if (k == 0 || stopped_probe) {
+                    if (threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
+                    break;
+                }
+                carry_known = true;
+            }
             ronly = false;  // not yet: full evaluation of the same iterate
         }
         // ---- residual, Jacobian and lane up-sweep.  Blocks that lie wholly
@@ -470,9 +491,10 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             publish_flag(A.flags + unit, it + 1);
         }
         if (at_cap) break;
-        V din = vzero<V>();
-        bool pred_stopped = true;
-        if (multi && k > 0) look_back<M, V>(A, ch, k, it, din, pred_stopped);
+        V din = carry_known ? din_probe : vzero<V>();
+        bool pred_stopped = carry_known ? stopped_probe : true;
+        if (multi && k > 0 && !carry_known) look_back<M, V>(A, ch, k, it, din, pred_stopped);
+        carry_known = false;
         if (cbit && pred_stopped) {
             if (multi && threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
             break;
@@ -617,7 +639,21 @@ __global__ void __launch_bounds__(kFoldThreads)
     uint32_t mx = 0u, itmax = 0u;
     unsigned long long sum = 0ull;
     const uint2 *r2 = reinterpret_cast<const uint2 *>(rec);
-    for (int64_t i = threadIdx.x; i < units; i += kFoldThreads) {
+    // four independent loads in flight per thread
+    constexpr int kU = 4;
+    int64_t i = threadIdx.x;
+    for (; i + (kU - 1) * kFoldThreads < units; i += kU * kFoldThreads) {
+        uint2 r[kU];
+#pragma unroll
+        for (int j = 0; j < kU; ++j) r[j] = r2[i + j * kFoldThreads];
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+            mx = max(mx, r[j].x);
+            itmax = max(itmax, r[j].y);
+            sum += r[j].y;
+        }
+    }
+    for (; i < units; i += kFoldThreads) {
         const uint2 r = r2[i];
         mx = max(mx, r.x);
         itmax = max(itmax, r.y);
