@@ -30,6 +30,10 @@
  *     caller; the library never allocates, frees or synchronises.  All work
  *     is enqueued on `stream` (a hipStream_t, NULL = default stream) and the
  *     call returns before it completes.  Outputs must not alias inputs.
+ *     A call enqueues kernel launches only (per-launch state is cleared by
+ *     a kernel, not by a memset), so it can be captured into a HIP graph;
+ *     a captured call keeps its workspace, and two replays that overlap in
+ *     time must not share one.
  *   - Layout: per-time-step planes are indexed (b, d, t); element offset of
  *     (b, d, t) = b*stride_b + d*stride_d + t*stride_t.  Planes of `u` (and
  *     of `du`) use u_stride_*; state, gradient and lambda planes use
