@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -72,8 +73,16 @@ def data_recipe(w):
 PROJECTION_ONLY = ("project.hpp", "inst_project.hip")
 
 
+def _code_only(text):
+    """C/C++ source without comments, indentation and blank lines: edits
+    to documentation do not change what is compiled."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.strip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_digest(family="solve"):
-    """Hash of the sources a kernel family is built from: "project" (the
+    """Hash of the code a kernel family is built from: "project" (the
     projection kernels and the ABI) or "solve" (everything else)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nonlinear_rnn_amd", "csrc")
@@ -84,8 +93,8 @@ def kernel_source_digest(family="solve"):
         names = [n for n in names if n not in PROJECTION_ONLY]
     paths = [os.path.join(csrc, n) for n in names] + [os.path.join(ROOT, "include", "pararnn.h")]
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update((os.path.basename(path) + _code_only(f.read())).encode())
     return h.hexdigest()[:16]
 
 

@@ -290,3 +290,16 @@ def test_workspace_cache_is_per_stream_and_bounded(monkeypatch):
         ws.get(16, "cpu", Stream(h))
     assert len(ws.buf) == pr.Workspace.MAX_STREAMS
     assert (None, 1) not in ws.buf                    # oldest streams dropped
+
+
+def test_kernel_digest_ignores_comments_and_layout():
+    """Traffic records stay valid across documentation edits: the digest
+    that ties them to the kernel sources hashes code only."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    a = bench._code_only("int f(int x) {  // add one\n    return x + 1; /* the\n result */\n}\n")
+    b = bench._code_only("/* doc */\nint f(int x) {\n\n  return x + 1;\n}")
+    assert a == b
+    assert a != bench._code_only("int f(int x) { return x + 2; }")
