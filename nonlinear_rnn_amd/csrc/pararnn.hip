@@ -20,6 +20,7 @@ namespace {
 
 constexpr int64_t kMaxIters = 1 << 20;  // flag encoding leaves room below kStopBase
 constexpr size_t kAlign = 256;
+constexpr int64_t kComputeUnits = 256;  // MI355X
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -119,6 +120,17 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
             sh->T > (int64_t)kWave * tab[0][0] * tab[0][1]) {
             K = 16;
             W = 8;
+        }
+        // Few channels in one block each: spread every channel over more
+        // waves at the same capacity (half the steps per lane, twice the
+        // waves) until the solve has about two waves per CU.  Each lane's
+        // serial chain per Newton pass shortens; nothing else changes.
+        if (kind == 0 && opt_k_w_unset(opt) && sh->T <= (int64_t)kWave * K * W) {
+            const int64_t channels = sh->B * sh->D;
+            while (K > 4 && W < 8 && channels * W < 2 * kComputeUnits) {
+                K /= 2;
+                W *= 2;
+            }
         }
     }
     const bool lstm = cell == PARARNN_LSTM;

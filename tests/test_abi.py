@@ -59,7 +59,10 @@ def test_plan_defaults():
     # one workgroup per channel up to 4096 steps, then time blocks
     assert pr.plan("gru", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
     assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (16, 8, 2)
-    assert pr.plan("gru", pr.make_shape(1, 1024, 64)) == (16, 1, 1)
+    # few channels: each spread over more waves at the same capacity
+    assert pr.plan("gru", pr.make_shape(1, 1024, 64)) == (4, 4, 1)
+    assert pr.plan("gru", pr.make_shape(1, 4096, 64)) == (8, 8, 1)
+    assert pr.plan("gru", pr.make_shape(1, 4096, 64), adjoint=True) == (8, 4, 2)  # unchanged
     assert pr.plan("gru", pr.make_shape(1, 1, 64)) == (1, 1, 1)
     assert pr.plan("lstm", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
     assert pr.plan("lstm", pr.make_shape(16, 2048, 4096)) == (16, 2, 1)
