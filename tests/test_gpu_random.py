@@ -1,4 +1,4 @@
-"""Randomised parity sweep: 48 configurations drawn from a fixed seed, each a
+"""Randomised parity sweeps: 48 solve configurations drawn from fixed seeds, each a
 mix the hand-written cases do not cover together: cell, projection dtype,
 batch, channels, a length that is rarely a tile multiple, forced or
 automatic tiling, channel- or time-major planes, and a cold or warm
@@ -110,3 +110,27 @@ def test_random_adjoint(i):
     for k in range(len(states)):
         grad_close(out["ds0"][k].cpu().numpy(), ds0[k])
         grad_close(out["lam"][k].cpu().numpy(), lam[k])
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_scan(i):
+    """The standalone scan on random configurations (state size, direction,
+    boundary value or none, tiling, time-major planes) against the oracle's
+    step-by-step recurrence; tolerance 1e-5 * max(1, max|x|)."""
+    from tests.test_gpu_scan import make, reference
+    c = draw(200 + i)
+    rng = np.random.default_rng(c["seed"])
+    S, reverse, with_x0 = int(rng.integers(1, 3)), bool(rng.random() < 0.5), bool(rng.random() < 0.7)
+    print(f"\n[scan case {i}] {c} S={S} reverse={reverse} x0={with_x0}", flush=True)
+    A, b, x0 = make(S, c["B"], c["T"], c["D"], c["seed"], with_x0)
+    ref = reference(A, b, x0, reverse)
+    At = [torch.from_numpy(v).to(DEV) for v in A]
+    bt = [torch.from_numpy(v).to(DEV) for v in b]
+    if c["time_major"]:
+        At = [v.transpose(1, 2).contiguous().transpose(1, 2) for v in At]
+        bt = [v.transpose(1, 2).contiguous().transpose(1, 2) for v in bt]
+    x0t = None if x0 is None else [torch.from_numpy(v).to(DEV) for v in x0]
+    x = pr.scan(At, bt, x0t, reverse=reverse, steps_per_lane=c["K"], waves_per_block=c["W"])
+    got = np.stack([v.cpu().numpy() for v in x])
+    scale = max(1.0, float(np.abs(ref).max()))
+    assert float(np.abs(got - ref).max()) <= 1e-5 * scale
