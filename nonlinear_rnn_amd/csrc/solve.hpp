@@ -264,7 +264,7 @@ __device__ __forceinline__ Map2 readlane_map(const Map2 &m, int src)
 // record load per lane instead of a chain of dependent loads.
 template <class M, class V>
 __device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_t k, int32_t it,
-                                          V &din, bool &pred_stopped)
+                                          V &din, bool &pred_stopped, int32_t &known)
 {
     constexpr int RF = MapRec<M>::kFloats;
     const int lane = threadIdx.x & (kWave - 1);
@@ -274,16 +274,23 @@ __device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_
     // Pass 1: from k-1 downwards, find the nearest block that stopped at or
     // before `it` (every block before it stopped no later); wait until each
     // block above it has published its record of this iteration.
+    // A stop flag never changes once set, so the nearest window's stop
+    // values seen in earlier iterations (`known`, one per lane) are reused:
+    // once every predecessor there has stopped, this pass issues no loads.
+    // Records behind such a flag were complete when it was first seen.
     int32_t start = 0;
     for (int32_t hi = k; hi > 0; hi -= kWave) {
         const int32_t lo = hi > kWave ? hi - kWave : 0;
         const int32_t j = lo + lane;
         const bool mine = j < hi;
-        int32_t v = mine ? load_flag(flags + j) : kStopBase;
+        const bool nearest = hi == k;
+        int32_t v = kStopBase;
+        if (mine) v = (nearest && known >= kStopBase) ? known : load_flag(flags + j);
         while (!__all(!mine || v >= it + 1)) {
             __builtin_amdgcn_s_sleep(1);
             if (mine && v < it + 1) v = load_flag(flags + j);
         }
+        if (nearest && mine && v >= kStopBase) known = v;
         const unsigned long long stopped =
             __ballot(mine && v >= kStopBase && v - kStopBase <= it);
         if (stopped) {
@@ -408,6 +415,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     int32_t it = 0;
     uint32_t bmx = 0;
     bool carry_known = false;  // the probe of this iteration already looked back
+    int32_t lb_known = 0;      // this lane's predecessor's stop flag, once seen
     V din_probe = vzero<V>();
     bool stopped_probe = true;
     bool ronly = false;  // this evaluation is the predicted last one
@@ -437,7 +445,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             if (it == A.cap) break;
             if (bmx < tolb) {
                 if (!multi) break;
-                if (k > 0) look_back<M, V>(A, ch, k, it, din_probe, stopped_probe);
+                if (k > 0) look_back<M, V>(A, ch, k, it, din_probe, stopped_probe, lb_known);
                 if (k == 0 || stopped_probe) {
                     if (threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
                     break;
@@ -493,7 +501,8 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         if (at_cap) break;
         V din = carry_known ? din_probe : vzero<V>();
         bool pred_stopped = carry_known ? stopped_probe : true;
-        if (multi && k > 0 && !carry_known) look_back<M, V>(A, ch, k, it, din, pred_stopped);
+        if (multi && k > 0 && !carry_known)
+            look_back<M, V>(A, ch, k, it, din, pred_stopped, lb_known);
         carry_known = false;
         if (cbit && pred_stopped) {
             if (multi && threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
