@@ -171,6 +171,32 @@ __device__ __forceinline__ M wave_scan_inclusive(M x)
     return x;
 }
 
+// One level of the 1x1 scan with the lane shift folded into the arithmetic
+// (two DPP instructions instead of two moves, two identity fills and two
+// products): b += a * b[src] with a missing source reading 0 (bound_ctrl),
+// then a *= a[src] with a missing source leaving the lane as it is.  Same
+// operations in the same order as compose(x, dpp_map(x)), so the same bits.
+// A DPP read needs two wait states after the VALU write of its source.
+#define PARARNN_SCAN1_LEVEL(DPP)                                                      \
+    asm volatile("s_nop 1\n\t"                                                         \
+                 "v_fmac_f32_dpp %1, %1, %0 " DPP " bound_ctrl:1\n\t"                   \
+                 "s_nop 1\n\t"                                                         \
+                 "v_mul_f32_dpp %0, %0, %0 " DPP "\n\t"                                 \
+                 "s_nop 1"                                                               \
+                 : "+v"(x.a), "+v"(x.b))
+template <>
+__device__ __forceinline__ Map1 wave_scan_inclusive<Map1>(Map1 x)
+{
+    PARARNN_SCAN1_LEVEL("row_shr:1 row_mask:0xf bank_mask:0xf");
+    PARARNN_SCAN1_LEVEL("row_shr:2 row_mask:0xf bank_mask:0xf");
+    PARARNN_SCAN1_LEVEL("row_shr:4 row_mask:0xf bank_mask:0xf");
+    PARARNN_SCAN1_LEVEL("row_shr:8 row_mask:0xf bank_mask:0xf");
+    PARARNN_SCAN1_LEVEL("row_bcast:15 row_mask:0xa bank_mask:0xf");
+    PARARNN_SCAN1_LEVEL("row_bcast:31 row_mask:0xc bank_mask:0xf");
+    return x;
+}
+#undef PARARNN_SCAN1_LEVEL
+
 // Value of lane l-1 (identity at lane 0): turns the inclusive scan into the
 // exclusive one.
 template <class M>
