@@ -423,17 +423,20 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     for (;; ++it) {
         if (ronly) {
             // ---- predicted last evaluation: residual and its maximum only
-            // The previous states pass through an empty asm: otherwise the
-            // compiler sees that a wrong guess re-evaluates the same gates
-            // and keeps all K steps' gate values live for the full evaluation.
+            // The gates of this pass and of a full pass of the same iterate
+            // after a wrong guess must not look alike to the compiler, or it
+            // keeps all K steps' gate values live into the full pass.  One
+            // side passes its states through an empty asm: the full pass, in
+            // place (one workgroup per channel: fewer registers and moves),
+            // or this one (time blocks: measured faster there).
             float mxf = 0.0f;
-            V prev = opaque(hin);
+            V prev = SINGLE ? hin : opaque(hin);
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) {
                 V rk = Cell::step_residual(cf, u[kk], prev, s[kk]);
                 if (!full) rk = keep_or_zero(rk, t0 + kk < T);
                 mxf = resmax(mxf, rk);
-                prev = opaque(s[kk]);
+                prev = SINGLE ? s[kk] : opaque(s[kk]);
             }
             const uint32_t wmx = wave_max_to_last(__float_as_uint(mxf));
             if (lane == kWave - 1) sm.slots[xp][wave].mx = wmx;
@@ -452,7 +455,13 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
                 }
                 carry_known = true;
             }
-            ronly = false;  // not yet: full evaluation of the same iterate
+            // not yet: full evaluation of the same iterate
+            if constexpr (SINGLE) {
+                hin = opaque(hin);
+#pragma unroll
+                for (int kk = 0; kk < K; ++kk) s[kk] = opaque(s[kk]);
+            }
+            ronly = false;
         }
         // ---- residual, Jacobian and lane up-sweep.  Blocks that lie wholly
         // inside [0, T) take a path without per-step masks; the ragged last
