@@ -383,7 +383,7 @@ def bench_speedup(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gru_f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
