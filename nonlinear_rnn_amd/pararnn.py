@@ -104,7 +104,8 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # plain ints: ctypes converts them for c_void_p parameters
+    return None if t is None else t.data_ptr()
 
 
 def _ptr_array(ts):
@@ -218,6 +219,7 @@ class Workspace:
 
 
 _ws = Workspace()
+_ws_sizes = {}  # solve workspace bytes by (cell, shape, strides, Newton options)
 
 
 def _stream_handle(stream):
@@ -246,9 +248,18 @@ def _solve(cell, u, a, s0, out, tol, max_iters, steps_per_lane, waves_per_block,
         out = _new_planes(S, B, T, D, _strides(u, "u"), dev)
         if init_from_output:
             raise ValueError("init_from_output needs the output planes")
-    shape = make_shape(B, T, D, _strides(u, "u"), _strides(out, "states"))
+    us, ss = _strides(u, "u"), _strides(out, "states")
+    shape = make_shape(B, T, D, us, ss)
     newton = make_newton(tol, max_iters, steps_per_lane, waves_per_block, init_from_output)
-    nws = workspace_bytes(cell, shape, newton)
+    # the size depends on these arguments only; cached so that small solves
+    # do not pay a second library call per launch
+    wkey = (cell, B, T, D, us, ss, tol, max_iters, steps_per_lane, waves_per_block,
+            bool(init_from_output))
+    nws = _ws_sizes.get(wkey)
+    if nws is None:
+        if len(_ws_sizes) >= 4096:
+            _ws_sizes.clear()
+        nws = _ws_sizes[wkey] = workspace_bytes(cell, shape, newton)
     ws = workspace if workspace is not None else _ws.get(nws, dev, stream)
     info_t = torch.empty(INFO_BYTES, dtype=torch.uint8, device=dev) if info else None
     args = [ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a)]
