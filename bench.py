@@ -1,19 +1,23 @@
-"""Bench: fused ParaGRU Newton solve, B=8 T=4096 D=1024 float32 on one GPU.
+"""Bench: fused ParaGRU Newton solve, bf16 projections, B=4 T=16384 D=4096,
+on one GPU, with the other four workloads measured in the same run.
 
 One step = one whole Newton solve (residual + Jacobian + scan + update +
-on-device convergence test, iterated to max|r| < 1e-6 or 20 updates) over
-the full batch, with the projections already resident in HBM.  For the
-forward + backward workload (--workload lstm_fwd_bwd) a step is the solve
-followed by the adjoint pass for upstream gradients dL/dh_t.
+on-device convergence test, iterated to max|r| < tol or the iteration cap)
+over the full batch, with the projections already resident in HBM.  For
+the forward + backward workload (lstm_fwd_bwd) a step is the solve followed
+by the adjoint pass for upstream gradients dL/dh_t.
 
-Prints ONE JSON line: throughput in hidden-state elements per second
-(B*T*D per solve); the dominant kernel's two roofs, algorithmic HBM bytes
-against the MI355X 8 TB/s and algorithmic VALU issue slots against the
-unpacked fp32 VALU rate, with `roofline` set to the one it runs closest to;
-and the CPU oracle timed on a bounded sample of the same workload on the
-host cores.
+Prints ONE JSON line for the headline workload (default gru_bf16_long, the
+largest): throughput in hidden-state elements per second (B*T*D per solve)
+from the wall clock of K back-to-back steps; the roofline of the dominant
+kernel, algorithmic HBM bytes per launch over its HIP-event average (the
+MALL evicted by a 512 MiB write before every launch) against the MI355X
+8 TB/s, with the VALU issue fraction as a secondary key; every other
+workload's figures under "configs"; and the CPU oracle timed on a bounded
+sample of the headline workload on all host cores and on one.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gru_f32]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gru_bf16_long]
+                    [--configs all|none|key,key]
 """
 import argparse
 import hashlib
@@ -39,6 +43,7 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # residual.  ParaGRU: 26 ops + 6 transcendentals per update pass, 12 + 6 on
 # the final pass; ParaLSTM (2x2 maps): 52 + 10, and 18 + 10.
 VALU_SLOTS = {"gru": (26 + 2 * 6, 12 + 2 * 6), "lstm": (52 + 2 * 10, 18 + 2 * 10)}
+HEADLINE = "gru_bf16_long"  # the largest workload
 METRIC = "hidden-state elems/sec per Newton solve (B·T·D) + % of MI355X HBM peak"
 
 
@@ -112,14 +117,14 @@ def measured_traffic(key):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s=12.0):
-    """The fp64 sequential oracle on a sample of channels, all host threads."""
-    import numpy as np
+def cpu_baseline(w, inp, budget_s=10.0):
+    """The fp64 sequential oracle on a sample of channels, timed on all host
+    threads (OpenMP over channels) and on one thread."""
     from oracle import sequential as seq
 
-    threads = seq.max_threads()
+    all_threads = seq.max_threads()
 
-    def run(n):
+    def run(n, threads):
         chans = [(i % w.B, (i * 7919) % w.D) for i in range(n)]
         sub_u, a_sub, s0_sub = seq.gather_channels(inp.u, inp.a, inp.s0, chans)
         t = time.perf_counter()
@@ -129,20 +134,28 @@ def cpu_baseline(w, inp, budget_s=12.0):
             seq.lstm_forward(sub_u, a_sub, s0_sub[0], s0_sub[1], threads)
         return time.perf_counter() - t
 
-    n = min(w.B * w.D, 4 * threads)
-    dt = run(n)
-    target = int(n * budget_s / max(dt, 1e-3))
-    n = max(n, min(w.B * w.D, target))
-    # repeat the sample until about budget_s of CPU time (core-seconds) is spent
-    reps, total = 0, 0.0
-    while reps == 0 or total * threads < budget_s:
-        total += run(n)
-        reps += 1
-    dt = total / reps
-    elems = n * w.T
-    return {"value": elems / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
+    def timed(threads):
+        n = min(w.B * w.D, 4 * threads)
+        dt = run(n, threads)
+        # a sample of about budget_s / 4 per run, repeated until about
+        # budget_s of wall time is spent
+        target = int(n * budget_s / 4 / max(dt, 1e-3))
+        n = max(n, min(w.B * w.D, target))
+        reps, total = 0, 0.0
+        while reps == 0 or total < budget_s:
+            total += run(n, threads)
+            reps += 1
+        dt = total / reps
+        return n, reps, dt, n * w.T / dt
+
+    n, reps, dt, rate = timed(all_threads)
+    n1, reps1, dt1, rate1 = timed(1)
+    return {"value": rate, "unit": "elem/s", "cores": all_threads, "kind": "oracle",
             "sample": f"{n} of {w.B * w.D} channels x T={w.T} (fp64 sequential step-by-step, "
-                      f"OpenMP over channels), mean of {reps} runs, {dt:.3f} s each"}
+                      f"OpenMP over channels), mean of {reps} runs, {dt:.3f} s each",
+            "single_thread": {"value": rate1, "unit": "elem/s", "cores": 1,
+                              "sample": f"{n1} channels x T={w.T}, mean of {reps1} runs, "
+                                        f"{dt1:.3f} s each"}}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -380,69 +393,32 @@ def bench_speedup(args):
             "points": points}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gru_f32")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--settle-ms", type=float, default=200.0,
-                    help="untimed back-to-back steps before the warm-up steps, for this long "
-                         "(ms of wall time), so that the GPU clocks reach their steady state")
-    ap.add_argument("--op", choices=["solve", "project", "checkpoint", "speedup"], default="solve",
-                    help="solve: the Newton solve (default); project: the input projection "
-                         "u = W x + b for the workload's shapes with I = D inputs; "
-                         "checkpoint: a training step one-piece vs checkpointed in time "
-                         "chunks (--chunk); speedup: Newton vs sequential application on "
-                         "the same GPU, 64 channels, growing T")
-    ap.add_argument("--chunk", type=int, default=512,
-                    help="time chunk of --op checkpoint")
-    ap.add_argument("--layout", choices=["channel", "time"], default="channel",
-                    help="channel: [B][D][T] planes (default); time: the gate blocks of one "
-                         "[B][T][G*D] projection tensor and [B][T][D] states")
-    ap.add_argument("--route", choices=["staged", "gather"], default="staged",
-                    help="with --layout time: staged (planes copied channel-major through "
-                         "the workspace, the default) or gather (a channel-major-size "
-                         "workspace, every step loaded on its own)")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="after the timed region, copy a buffer of this many MiB three "
-                         "times (plain device copy used to calibrate HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
-              "channels are independent, so the path shards over B*D with no exchange, "
-              "but no multi-GPU run is part of it.", file=sys.stderr)
-        sys.exit(2)
+def flush_mall(buf):
+    """Write the whole eviction buffer (>= 512 MB, twice the 256 MB MALL), so
+    that the next launch finds none of its inputs in the last-level cache."""
+    buf.fill_(1.0)
 
+
+def measure_solve(w, key, args, flush_buf, headline):
+    """One workload: convergence report, then the contract's timed region
+    (K back-to-back steps, wall clock, HIP events around every launch on its
+    stream), then K more steps with a MALL-evicting write before each one
+    (outside the event pair) for the roofline."""
+    import numpy as np
     import torch
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
     from nonlinear_rnn_amd import pararnn as pr
-    from nonlinear_rnn_amd.inputs import WORKLOADS, workload_inputs
+    from nonlinear_rnn_amd.inputs import workload_inputs
 
-    w = WORKLOADS[args.workload]
-    if args.op == "project":
-        print(json.dumps(bench_project(w, args)), flush=True)
-        return
-    if args.op == "checkpoint":
-        print(json.dumps(bench_checkpoint(w, args)), flush=True)
-        return
-    if args.op == "speedup":
-        print(json.dumps(bench_speedup(args)), flush=True)
-        return
     inp = workload_inputs(w)
     dev = "cuda:0"
     if inp.u_bf16 is not None:
-        import numpy as np
         u = [torch.from_numpy(p.view(np.int16)).view(torch.bfloat16).to(dev) for p in inp.u_bf16]
     else:
         u = [torch.from_numpy(p).to(dev) for p in inp.u]
     a = torch.from_numpy(inp.a).to(dev)
     s0 = [torch.from_numpy(p).to(dev) for p in inp.s0]
     out = [torch.empty((w.B, w.D, w.T), dtype=torch.float32, device=dev) for _ in range(w.S)]
-    time_major = args.layout == "time"
+    time_major = headline and args.layout == "time"
     if time_major:
         # one [B][T][G*D] tensor (what a Linear over [B][T][I] inputs gives),
         # passed per gate as strided views; states [B][T][D]
@@ -473,6 +449,7 @@ def main():
                              info=info, workspace=ws_solve, stream=stream)[1]
 
     adj_out = None
+    gs = None
     if w.adjoint:
         gh = torch.from_numpy(inp.dh).to(dev)
         if time_major:
@@ -503,83 +480,68 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps; every launch bracketed by HIP events on its stream
     nev = 3 if w.adjoint else 2
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-           for _ in range(args.steps)]
+
+    def events():
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+                for _ in range(args.steps)]
+
+    def run(evs, flush):
+        for ev in evs:
+            if flush:
+                flush_mall(flush_buf)
+            ev[0].record(stream)
+            solve(False)
+            ev[1].record(stream)
+            if w.adjoint:
+                backward()
+                ev[2].record(stream)
+
+    # the timed region: K back-to-back steps
+    evs = events()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for ev in evs:
-        ev[0].record(stream)
-        solve(False)
-        ev[1].record(stream)
-        if w.adjoint:
-            backward()
-            ev[2].record(stream)
+    run(evs, False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    # the roofline region: K steps, the MALL evicted before each one
+    cold = events()
+    torch.cuda.synchronize()
+    run(cold, True)
+    torch.cuda.synchronize()
 
     def kernel_stats(i, name, nbytes):
-        ms = [ev[i].elapsed_time(ev[i + 1]) for ev in evs]
+        warm = [ev[i].elapsed_time(ev[i + 1]) for ev in evs]
+        ms = [ev[i].elapsed_time(ev[i + 1]) for ev in cold]
         avg = sum(ms) / len(ms)
-        return {"kernel": name, "ms_avg": avg, "ms_min": min(ms), "bytes": nbytes,
-                "achieved": nbytes / (avg * 1e-3) / 1e9}
+        return {"kernel": name, "ms_avg": avg, "ms_min": min(ms),
+                "ms_avg_back_to_back": sum(warm) / len(warm), "bytes": nbytes,
+                "achieved": nbytes / (avg * 1e-3) / 1e9,
+                "hbm_frac": nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
     kernels = [kernel_stats(0, "newton_kernel", algorithmic_bytes(w))]
     # VALU issue slots of the solve: every unit runs its updates plus one
     # final residual pass (iters_mean = updates per unit)
     upd, fin = VALU_SLOTS[w.cell]
-    kernels[0]["valu_ops"] = w.N * (info["iters_mean"] * upd + fin)
+    ops = w.N * (info["iters_mean"] * upd + fin)
+    tops = ops / (kernels[0]["ms_avg"] * 1e-3) / 1e12
+    kernels[0]["valu"] = {"achieved": tops, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
+                          "frac": tops / VALU_PEAK_TOPS, "ops_per_launch": ops,
+                          "ops": "algorithmic VALU lane-op issue slots (exp2/rcp = 2)"}
     if w.adjoint:
         kernels.append(kernel_stats(1, "adjoint_kernel", adjoint_bytes(w)))
-    dom = max(kernels, key=lambda k: k["ms_avg"])
-    abytes, kavg_ms, kmin_ms = dom["bytes"], dom["ms_avg"], dom["ms_min"]
-    hbm = {"achieved": dom["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": dom["achieved"] / HBM_PEAK_GBS}
-    valu = None
-    if "valu_ops" in dom:
-        tops = dom["valu_ops"] / (kavg_ms * 1e-3) / 1e12
-        valu = {"achieved": tops, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
-                "frac": tops / VALU_PEAK_TOPS, "ops_per_launch": dom["valu_ops"],
-                "ops": "algorithmic VALU lane-op issue slots (exp2/rcp = 2)"}
-    # the binding roof is the one the kernel runs closest to
-    bound = "alu" if valu is not None and valu["frac"] > hbm["frac"] else "hbm"
-    roof = valu if bound == "alu" else hbm
-    traffic = measured_traffic(args.workload + (f"_time_major_{args.route}" if time_major else ""))
     K, W, nb = pr.plan(w.cell, pr.make_shape(w.B, w.T, w.D))
-    line = {
-        "metric": METRIC,
-        "value": w.N / (ms_per_step * 1e-3),
-        "unit": "elem/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "settle": {"ms": args.settle_ms, "steps": n_settle,
-                   "kind": "untimed back-to-back steps before the warm-up, so that the "
-                           "GPU clocks reach their steady state"},
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16-in/f32" if w.u_dtype == "bf16" else "f32",
-        "data": data_recipe(w),
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol,
-                   "layout": ("time-major: u gate blocks of one [B][T][G*D] tensor, "
-                              f"states [B][T][D]; {args.route} route") if time_major else
-                             "channel-major [B][D][T] planes",
-                   "max_iters": w.max_iters, "seed": w.seed, "tiling": {"K": K, "W": W,
-                   "time_blocks": nb}, "newton_updates": info["iters"],
-                   "newton_updates_mean": info["iters_mean"], "converged": info["converged"],
-                   "max_abs_res": info["max_abs_res"]},
-        "roofline": {"bound": bound, "achieved": roof["achieved"], "peak": roof["peak"],
-                     "unit": roof["unit"], "frac": roof["frac"],
-                     "traffic": traffic, "algorithmic_bytes": abytes,
-                     "kernel": dom["kernel"], "kernel_ms_avg": kavg_ms,
-                     "kernel_ms_min": kmin_ms, "hbm": hbm, "valu": valu},
+    res = {
+        "workload": w.name, "B": w.B, "T": w.T, "D": w.D, "N": w.N,
+        "ms_per_step": ms_per_step, "elem_per_s": w.N / (ms_per_step * 1e-3),
+        "tol": w.tol, "max_iters": w.max_iters, "seed": w.seed,
+        "tiling": {"K": K, "W": W, "time_blocks": nb},
+        "newton_updates": info["iters"], "newton_updates_mean": info["iters_mean"],
+        "converged": info["converged"], "max_abs_res": info["max_abs_res"],
+        "settle": {"ms": args.settle_ms, "steps": n_settle},
+        "kernels": kernels,
     }
-    if len(kernels) > 1:
-        line["kernels"] = kernels
     # context: the same trajectory by step-by-step application on the GPU
     # (one lane per channel), the baseline of the pages' parallel speed-up
     seq_out = [torch.empty_like(x) for x in out]
@@ -593,20 +555,158 @@ def main():
         e1.record(stream)
     torch.cuda.synchronize()
     seq_ms = sorted(e0.elapsed_time(e1) for e0, e1 in sev)[len(sev) // 2]
-    line["gpu_sequential"] = {"value": w.N / (seq_ms * 1e-3), "unit": "elem/s", "ms": seq_ms,
-                              "newton_kernel_speedup": seq_ms / kernels[0]["ms_avg"],
-                              "kind": "step-by-step application, one lane per channel"}
+    res["gpu_sequential"] = {"ms": seq_ms, "elem_per_s": w.N / (seq_ms * 1e-3),
+                             "newton_kernel_speedup": seq_ms / kernels[0]["ms_avg"],
+                             "kind": "step-by-step application, one lane per channel"}
     del seq_out
-    if args.copy_mib:
+    if headline and args.copy_mib:
         n = args.copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        line["copy_calibration_bytes"] = n * 4
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp)
+        res["copy_calibration_bytes"] = n * 4
+    if headline and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp)
+    del u, a, s0, out, adj_out, gs, inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="the workload the line's value and roofline are quoted on "
+                         f"(default {HEADLINE}, the largest)")
+    ap.add_argument("--configs", default="all",
+                    help="other workloads measured in the same run and nested under "
+                         "'configs': all (default), none, or a comma list of keys")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed back-to-back steps before the warm-up steps, for this long "
+                         "(ms of wall time), so that the GPU clocks reach their steady state")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="size of the buffer written before every step of the roofline "
+                         "region (evicts the 256 MB MALL); at least 512")
+    ap.add_argument("--op", choices=["solve", "project", "checkpoint", "speedup"], default="solve",
+                    help="solve: the Newton solve (default); project: the input projection "
+                         "u = W x + b for the workload's shapes with I = D inputs; "
+                         "checkpoint: a training step one-piece vs checkpointed in time "
+                         "chunks (--chunk); speedup: Newton vs sequential application on "
+                         "the same GPU, 64 channels, growing T")
+    ap.add_argument("--chunk", type=int, default=512,
+                    help="time chunk of --op checkpoint")
+    ap.add_argument("--layout", choices=["channel", "time"], default="channel",
+                    help="channel: [B][D][T] planes (default); time: the gate blocks of one "
+                         "[B][T][G*D] projection tensor and [B][T][D] states (the headline "
+                         "workload only)")
+    ap.add_argument("--route", choices=["staged", "gather"], default="staged",
+                    help="with --layout time: staged (planes copied channel-major through "
+                         "the workspace, the default) or gather (a channel-major-size "
+                         "workspace, every step loaded on its own)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, copy a buffer of this many MiB three "
+                         "times (plain device copy used to calibrate HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for {args.gpus}); "
+              "channels are independent, so the path shards over B*D with no exchange, "
+              "but no multi-GPU run is part of it.", file=sys.stderr)
+        sys.exit(2)
+    if args.flush_mib < 512:
+        ap.error("--flush-mib must be at least 512 (twice the MALL)")
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from nonlinear_rnn_amd import pararnn as pr  # noqa: F401  (fails loudly if not built)
+    from nonlinear_rnn_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    if args.op == "project":
+        print(json.dumps(bench_project(w, args)), flush=True)
+        return
+    if args.op == "checkpoint":
+        print(json.dumps(bench_checkpoint(w, args)), flush=True)
+        return
+    if args.op == "speedup":
+        print(json.dumps(bench_speedup(args)), flush=True)
+        return
+    if args.configs == "all":
+        others = [k for k in WORKLOADS if k != args.workload]
+    elif args.configs == "none":
+        others = []
+    else:
+        others = [k for k in args.configs.split(",") if k and k != args.workload]
+        for k in others:
+            if k not in WORKLOADS:
+                ap.error(f"unknown workload {k!r}")
+    flush_buf = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32,
+                            device="cuda:0")
+    head = measure_solve(w, args.workload, args, flush_buf, headline=True)
+    print(f"bench.py: {args.workload} {head['ms_per_step']:.4f} ms/step, kernel "
+          f"{head['kernels'][0]['ms_avg']:.4f} ms", file=sys.stderr, flush=True)
+    nested = {}
+    for key in others:
+        r = measure_solve(WORKLOADS[key], key, args, flush_buf, headline=False)
+        nested[key] = r
+        print(f"bench.py: {key} {r['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
+
+    time_major = args.layout == "time"
+    dom = max(head["kernels"], key=lambda k: k["ms_avg"])
+    traffic = measured_traffic(args.workload + (f"_time_major_{args.route}" if time_major else ""))
+    line = {
+        "metric": METRIC,
+        "value": head["elem_per_s"],
+        "unit": "elem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": head["settle"]["steps"],
+                   "kind": "untimed back-to-back steps before the warm-up, so that the "
+                           "GPU clocks reach their steady state"},
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/f32" if w.u_dtype == "bf16" else "f32",
+        "data": data_recipe(w),
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol,
+                   "layout": ("time-major: u gate blocks of one [B][T][G*D] tensor, "
+                              f"states [B][T][D]; {args.route} route") if time_major else
+                             "channel-major [B][D][T] planes",
+                   "max_iters": w.max_iters, "seed": w.seed, "tiling": head["tiling"],
+                   "newton_updates": head["newton_updates"],
+                   "newton_updates_mean": head["newton_updates_mean"],
+                   "converged": head["converged"], "max_abs_res": head["max_abs_res"]},
+        # HBM is the roof the metric is quoted against: algorithmic bytes per
+        # launch over the kernel's HIP-event average with the MALL evicted
+        # before every launch; the VALU issue fraction rides along
+        "roofline": {"bound": "hbm", "achieved": dom["achieved"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": traffic,
+                     "algorithmic_bytes": dom["bytes"], "kernel": dom["kernel"],
+                     "kernel_ms_avg": dom["ms_avg"], "kernel_ms_min": dom["ms_min"],
+                     "kernel_ms_avg_back_to_back": dom["ms_avg_back_to_back"],
+                     "timing": f"HIP events on the launch stream, {args.steps} launches, "
+                               f"a {args.flush_mib} MiB write before each (outside the "
+                               "event pair)",
+                     "valu": dom.get("valu")},
+        "kernels": head["kernels"],
+        "gpu_sequential": head["gpu_sequential"],
+        "configs": {args.workload: {k: head[k] for k in ("workload", "ms_per_step", "elem_per_s",
+                                                         "newton_updates_mean", "kernels")}},
+    }
+    for key, r in nested.items():
+        line["configs"][key] = r
+    if "copy_calibration_bytes" in head:
+        line["copy_calibration_bytes"] = head["copy_calibration_bytes"]
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
     print(json.dumps(line), flush=True)
 
 
