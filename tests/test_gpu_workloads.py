@@ -1,12 +1,21 @@
 """The five workloads at full size, in the launch configuration the bench
-times (automatic tiling), checked against the oracle on sampled channels
-(each channel's trajectory depends on no other channel, so the oracle can
-run on a sample) and via properties that hold at any size (converged,
-max |r| < tol everywhere, no NaN).
+times (automatic tiling), compared with the oracle on every channel.
 
-Tolerances: 1e-5 max-abs for float32 states; the bf16-projection workload
-is gated at 2e-2 against the oracle on the unrounded float32 draw, with a
-diagnostic against the oracle on the rounded values; gradients at
+The oracle runs one batch row at a time (every channel's trajectory depends
+on no other channel, so a row is a complete sub-problem), which bounds the
+host memory at full size; besides the element-wise comparison the tests
+check the properties that hold at any size (converged, max |r| < tol
+everywhere, no NaN).
+
+Tolerances: 1e-5 max-abs for float32 states.  The bf16-projection workload
+is gated at 2e-2 against the oracle on the unrounded float32 draw; its
+diagnostic against the oracle on the rounded values (the inputs the device
+sees) is bounded by the stopping rule itself: a trajectory with
+max |r_t| < tol differs from the zero of r by e_t = r_t + J_t e_{t-1} to
+first order ("Параллельность RNN?", forpes.ru, §1.1-1.3), so
+|e_t| <= tol * kappa with kappa = max_t sum_k prod_{j=k+1..t} |J_j| taken
+along the oracle trajectory; the test computes kappa over every channel
+and allows tol * kappa plus 1e-6 of float32 rounding.  Gradients at
 1e-5 * max(1, max|reference|) per tensor.
 """
 import numpy as np
@@ -14,19 +23,12 @@ import pytest
 import torch
 
 from nonlinear_rnn_amd import pararnn as pr
-from nonlinear_rnn_amd.inputs import WORKLOADS, workload_inputs
+from nonlinear_rnn_amd.inputs import WORKLOADS, bf16_to_f32, workload_inputs
+from oracle import deer
 from oracle import sequential as seq
 from tests.gpu_util import DEV, dev_inputs
 
-pytestmark = pytest.mark.gpu
-
-
-def sample_channels(B, D, n, seed):
-    rng = np.random.default_rng(seed)
-    ch = {(0, 0), (B - 1, D - 1), (0, D - 1), (B - 1, 0)}
-    while len(ch) < n:
-        ch.add((int(rng.integers(B)), int(rng.integers(D))))
-    return sorted(ch)
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
 
 def run_forward(w, inp):
@@ -40,19 +42,43 @@ def run_forward(w, inp):
     return (u, a, s0), states, pr.read_info(info)
 
 
-def oracle_on(inp, chans, rounded):
-    u = inp.u_rounded if rounded else inp.u
-    sub_u, a_sub, s0_sub = seq.gather_channels(u, inp.a, inp.s0, chans)
+def row_u(inp, b, rounded):
+    """Batch row b of the projections as float32 planes [1][D][T]: the
+    values the device sees (bf16 widened exactly), or the unrounded draw."""
+    if rounded and inp.u_bf16 is not None:
+        return [bf16_to_f32(p[b:b + 1]) for p in inp.u_bf16]
+    return [np.ascontiguousarray(p[b:b + 1]) for p in inp.u]
+
+
+def oracle_row(inp, b, rounded):
+    u = row_u(inp, b, rounded)
+    s0 = [np.ascontiguousarray(s[b:b + 1]) for s in inp.s0]
     if inp.cell == "gru":
-        return [seq.gru_forward(sub_u, a_sub, s0_sub[0])[0]]
-    c, h = seq.lstm_forward(sub_u, a_sub, s0_sub[0], s0_sub[1])
+        return [seq.gru_forward(u, inp.a, s0[0])[0]]
+    c, h = seq.lstm_forward(u, inp.a, s0[0], s0[1])
     return [c[0], h[0]]
 
 
-def gpu_on(states, chans):
-    bs = torch.tensor([c[0] for c in chans], device=DEV)
-    ds = torch.tensor([c[1] for c in chans], device=DEV)
-    return [s[bs, ds].cpu().numpy() for s in states]
+def gru_kappa(inp, b, h):
+    """max over channels and steps of sum_k prod_{j=k+1..t} |J_j| along the
+    oracle trajectory h ([D][T]) of batch row b, with the oracle's Jacobian."""
+    u = np.stack([p[0] for p in row_u(inp, b, True)], axis=-1).astype(np.float64)
+    hp = np.concatenate([inp.s0[0][b][:, None].astype(np.float64), h[:, :-1]], axis=1)
+    aJ = np.abs(deer.GRU.jac(hp[..., None], u, inp.a.T.astype(np.float64)[:, None, :])[..., 0, 0])
+    kap = np.zeros(h.shape[0])
+    kmax = 0.0
+    for t in range(h.shape[1]):
+        kap = 1.0 + aJ[:, t] * kap
+        kmax = max(kmax, float(kap.max()))
+    return kmax
+
+
+def gpu_row(states, b):
+    return [s[b].cpu().numpy() for s in states]
+
+
+def max_abs_diff(got, ref):
+    return max(float(np.abs(g.astype(np.float64) - r).max()) for g, r in zip(got, ref))
 
 
 @pytest.mark.parametrize("key", ["gru_small", "gru_f32", "lstm_f32", "gru_bf16_long"])
@@ -65,19 +91,22 @@ def test_workload_forward(key):
     assert info["iters"] <= w.max_iters
     for s in states:
         assert bool(torch.isfinite(s).all())
-    n = w.B * w.D if w.B * w.D <= 64 else 48
-    chans = sample_channels(w.B, w.D, n, w.seed)
-    got = gpu_on(states, chans)
+    err = err_gate = 0.0
+    kappa = 0.0
+    for b in range(w.B):
+        got = gpu_row(states, b)
+        ref = oracle_row(inp, b, True)
+        err = max(err, max_abs_diff(got, ref))
+        if w.u_dtype == "bf16":
+            err_gate = max(err_gate, max_abs_diff(got, oracle_row(inp, b, False)))
+            kappa = max(kappa, gru_kappa(inp, b, ref[0]))
+    print(f"\n{key}: {w.B * w.D} of {w.B * w.D} channels, iters={info['iters']} "
+          f"mean={info['iters_mean']:.2f} err={err:.3e}"
+          + (f" gate_err={err_gate:.3e} kappa={kappa:.2f}" if w.u_dtype == "bf16" else ""))
     if w.u_dtype == "bf16":
-        err_gate = max(float(np.abs(g - r).max()) for g, r in zip(got, oracle_on(inp, chans, False)))
-        err_diag = max(float(np.abs(g - r).max()) for g, r in zip(got, oracle_on(inp, chans, True)))
-        print(f"\n{key}: iters={info['iters']} mean={info['iters_mean']:.2f} "
-              f"gate_err={err_gate:.3e} diag_err={err_diag:.3e}")
         assert err_gate < 2e-2
-        assert err_diag < 1e-4
+        assert err <= w.tol * kappa + 1e-6, (err, kappa)
     else:
-        err = max(float(np.abs(g - r).max()) for g, r in zip(got, oracle_on(inp, chans, True)))
-        print(f"\n{key}: iters={info['iters']} mean={info['iters_mean']:.2f} err={err:.3e}")
         assert err < 1e-5
 
 
@@ -89,31 +118,31 @@ def test_workload_lstm_forward_and_adjoint():
     dh = torch.from_numpy(inp.dh).to(DEV)
     out = pr.adjoint("lstm", u, a, s0, states, [None, dh])
     torch.cuda.synchronize()
-    # sampled channels: every batch row of a few d, so that da[:, d] is exact
-    rng = np.random.default_rng(55)
-    dsel = sorted({0, w.D - 1} | set(int(x) for x in rng.integers(0, w.D, 6)))
-    chans = [(b, d) for d in dsel for b in range(w.B)]
-    sub_u, a_sub, s0_sub = seq.gather_channels(inp.u, inp.a, inp.s0, chans)
-    dh_sub = inp.dh[[c[0] for c in chans], [c[1] for c in chans]][None]
-    ref = seq.lstm_bptt(sub_u, a_sub, s0_sub[0], s0_sub[1], dh_sub)
-    fwd_err = max(float(np.abs(g - r).max()) for g, r in
-                  zip(gpu_on(states, chans), [ref["c"][0], ref["h"][0]]))
-    assert fwd_err < 1e-5
-    errs = {}
-    for g in range(4):
-        got = gpu_on([out["du"][g]], chans)[0]
-        r = ref["du"][g][0]
-        errs[f"du{g}"] = float(np.abs(got - r).max()) / max(1.0, float(np.abs(r).max()))
-    da_ref = np.zeros((4, len(dsel)))
-    for j, d in enumerate(dsel):
-        idx = [i for i, c in enumerate(chans) if c[1] == d]
-        da_ref[:, j] = ref["da"][:, idx].sum(axis=1)
-    da_got = out["da"][:, dsel].cpu().numpy()
+    fwd_err = 0.0
+    diff = {k: 0.0 for k in ("du0", "du1", "du2", "du3", "dc0", "dh0")}
+    mref = dict(diff)
+    da_ref = np.zeros((4, w.D))
+    for b in range(w.B):
+        u_b = row_u(inp, b, True)
+        ref = seq.lstm_bptt(u_b, inp.a, inp.s0[0][b:b + 1], inp.s0[1][b:b + 1],
+                            inp.dh[b:b + 1])
+        fwd_err = max(fwd_err, max_abs_diff(gpu_row(states, b), [ref["c"][0], ref["h"][0]]))
+        for g in range(4):
+            got = out["du"][g][b].cpu().numpy().astype(np.float64)
+            r = ref["du"][g][0]
+            diff[f"du{g}"] = max(diff[f"du{g}"], float(np.abs(got - r).max()))
+            mref[f"du{g}"] = max(mref[f"du{g}"], float(np.abs(r).max()))
+        for c, k in enumerate(("dc0", "dh0")):
+            got = out["ds0"][c][b].cpu().numpy().astype(np.float64)
+            r = ref[k][0]
+            diff[k] = max(diff[k], float(np.abs(got - r).max()))
+            mref[k] = max(mref[k], float(np.abs(r).max()))
+        da_ref += ref["da"]
+    errs = {k: diff[k] / max(1.0, mref[k]) for k in diff}
+    da_got = out["da"].cpu().numpy().astype(np.float64)
     errs["da"] = float(np.abs(da_got - da_ref).max()) / max(1.0, float(np.abs(da_ref).max()))
-    for c, key in enumerate(["dc0", "dh0"]):
-        got = gpu_on([out["ds0"][c].unsqueeze(-1)], chans)[0][:, 0]
-        r = ref[key][0]
-        errs[key] = float(np.abs(got - r).max()) / max(1.0, float(np.abs(r).max()))
-    print("\nlstm_fwd_bwd relative errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    print(f"\nlstm_fwd_bwd: {w.B * w.D} of {w.B * w.D} channels, forward err {fwd_err:.3e}, "
+          "relative gradient errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert fwd_err < 1e-5
     for k, v in errs.items():
         assert v <= 1e-5, (k, v)
