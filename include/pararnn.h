@@ -167,8 +167,15 @@ pararnn_status_t pararnn_solve_lstm(const pararnn_shape_t *shape, const void *co
  *   s      : S pointers to [B][D][T] converged states s_1..s_T
  *   gs     : S pointers to [B][D][T] upstream gradients dL/ds_t; an entry
  *            may be NULL, meaning zero (e.g. dL/dc_t for an LSTM)
+ *   gs_end : NULL, or S pointers to [B][D] (an entry may be NULL = zero):
+ *            a gradient added to dL/ds_T at the last step — what a
+ *            continuation of the sequence sends back, i.e. the ds0 of the
+ *            adjoint of the next time chunk (A_{T+1}^T lam_{T+1} of the
+ *            uncut recurrence), so a sequence cut into chunks is
+ *            differentiated chunk by chunk, last chunk first
  *   du     : G pointers to [B][D][T] float32 outputs dL/du (u_stride_*)
  *   da     : [G][D] float32 output dL/da (summed over batch and time)
+ *   da_accumulate : 0: da = the sum; 1: da += the sum (chunk by chunk)
  *   ds0    : S pointers to [B][D] float32 outputs dL/ds_0
  *   lam    : NULL, or S pointers to [B][D][T] float32 outputs lam_t
  *   opt    : only steps_per_lane / waves_per_block are read (may be NULL)
@@ -178,7 +185,8 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
                                  const void *const *u, pararnn_dtype_t u_dtype,
                                  const float *a, const float *const *s0,
                                  const float *const *s, const float *const *gs,
-                                 float *const *du, float *da, float *const *ds0,
+                                 const float *const *gs_end, float *const *du, float *da,
+                                 int32_t da_accumulate, float *const *ds0,
                                  float *const *lam, const pararnn_newton_t *opt,
                                  void *ws, size_t ws_bytes, void *stream);
 

@@ -26,8 +26,10 @@ struct AdjArgs {
     const float *s0[2];
     const float *s[2];
     const float *gs[2];
+    const float *gend[2];  // [B][D] added to g at the last step, or null
     float *du[4];
     float *da;
+    int32_t da_acc;        // 1: da += the new sum, 0: da = the new sum
     float *ds0[2];
     float *lam[2];
     int64_t B, T, D;
@@ -232,6 +234,13 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
 #pragma unroll
                 for (int kk = 0; kk < K; ++kk) tmp[kk] = 0.0f;
             }
+            // the gradient a continuation of the sequence sends back to s_T
+            if (A.gend[c] && t0 <= T - 1 && T - 1 < t0 + K) {
+                const float e = A.gend[c][b * A.D + d];
+#pragma unroll
+                for (int kk = 0; kk < K; ++kk)
+                    if (t0 + kk == T - 1) tmp[kk] += e;
+            }
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) vset(gv[kk], c, tmp[kk]);
         }
@@ -344,15 +353,16 @@ __global__ void adjoint_init_kernel(AdjArgs A, int32_t S, int32_t G, int64_t uni
         if (A.T == 0) {
             // no steps: every gradient that exists is zero
             for (int g = 0; g < G; ++g) A.da_part[i * G + g] = 0.0f;
+            // (s_T is s_0 itself: a continuation's gradient passes through)
             const int64_t ch = i / A.nb;
             if (i - ch * A.nb == 0)
-                for (int c = 0; c < S; ++c) A.ds0[c][ch] = 0.0f;
+                for (int c = 0; c < S; ++c) A.ds0[c][ch] = A.gend[c] ? A.gend[c][ch] : 0.0f;
         }
     }
 }
 
 // da[g][d] = sum over batch rows b and time blocks k of the partials, in
-// that fixed order.
+// that fixed order (added to the value already in da when da_acc is set).
 __global__ void da_reduce_kernel(AdjArgs A, int32_t G)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -361,7 +371,7 @@ __global__ void da_reduce_kernel(AdjArgs A, int32_t G)
     float acc = 0.0f;
     for (int64_t b = 0; b < A.B; ++b)
         for (int32_t k = 0; k < A.nb; ++k) acc += A.da_part[((b * A.D + d) * A.nb + k) * G + g];
-    A.da[i] = acc;
+    A.da[i] = A.da_acc ? A.da[i] + acc : acc;
 }
 
 #endif

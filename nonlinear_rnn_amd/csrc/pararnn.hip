@@ -567,7 +567,8 @@ pararnn_status_t scan_core(int32_t state_size, const pararnn_shape_t *shape,
 pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
                               const void *const *u, pararnn_dtype_t u_dtype, const float *a,
                               const float *const *s0, const float *const *s,
-                              const float *const *gs, float *const *du, float *da,
+                              const float *const *gs, const float *const *gs_end,
+                              float *const *du, float *da, int32_t da_accumulate,
                               float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
                               void *ws, size_t ws_bytes, void *stream);
 
@@ -868,7 +869,8 @@ pararnn_status_t pararnn_solve_lstm(const pararnn_shape_t *shape, const void *co
 pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *shape,
                                  const void *const *u, pararnn_dtype_t u_dtype, const float *a,
                                  const float *const *s0, const float *const *s,
-                                 const float *const *gs, float *const *du, float *da,
+                                 const float *const *gs, const float *const *gs_end,
+                                 float *const *du, float *da, int32_t da_accumulate,
                                  float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
                                  void *ws, size_t ws_bytes, void *stream)
 {
@@ -885,8 +887,8 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
     for (int g = 0; g < G && staged; ++g) staged = u[g] && du[g];
     for (int c = 0; c < S && staged; ++c) staged = s[c] && (!lam || lam[c]);
     if (!staged)
-        return adjoint_core(cell, shape, u, u_dtype, a, s0, s, gs, du, da, ds0, lam, opt, ws,
-                            ws_bytes, stream);
+        return adjoint_core(cell, shape, u, u_dtype, a, s0, s, gs, gs_end, du, da, da_accumulate,
+                            ds0, lam, opt, ws, ws_bytes, stream);
 
     hipStream_t strm = static_cast<hipStream_t>(stream);
     char *base = static_cast<char *>(ws);
@@ -935,8 +937,8 @@ pararnn_status_t pararnn_adjoint(pararnn_cell_t cell, const pararnn_shape_t *sha
         sh2.s_stride_d = dT;
         sh2.s_stride_t = 1;
     }
-    st = adjoint_core(cell, &sh2, u2, u_dtype, a, s0, s2, gs2, du2, da, ds0, lam ? lam2 : nullptr,
-                      opt, ws, ws_bytes, stream);
+    st = adjoint_core(cell, &sh2, u2, u_dtype, a, s0, s2, gs2, gs_end, du2, da, da_accumulate,
+                      ds0, lam ? lam2 : nullptr, opt, ws, ws_bytes, stream);
     if (st != PARARNN_OK) return st;
     for (int g = 0; g < G && sg.u; ++g) {
         const TransArgs t = plane_copy(du2[g], shape, dDT, dT, 1, du[g], shape->u_stride_b,
@@ -958,12 +960,14 @@ namespace {
 pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
                               const void *const *u, pararnn_dtype_t u_dtype, const float *a,
                               const float *const *s0, const float *const *s,
-                              const float *const *gs, float *const *du, float *da,
+                              const float *const *gs, const float *const *gs_end,
+                              float *const *du, float *da, int32_t da_accumulate,
                               float *const *ds0, float *const *lam, const pararnn_newton_t *opt,
                               void *ws, size_t ws_bytes, void *stream)
 {
     if (cell != PARARNN_GRU && cell != PARARNN_LSTM) return PARARNN_ERR_INVALID;
     if (u_dtype != PARARNN_F32 && u_dtype != PARARNN_BF16) return PARARNN_ERR_UNSUPPORTED;
+    if (da_accumulate != 0 && da_accumulate != 1) return PARARNN_ERR_INVALID;
     Plan pl;
     pararnn_status_t st = make_plan(cell, shape, opt, 1, pl);
     if (st != PARARNN_OK) return st;
@@ -991,11 +995,13 @@ pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
         A.s0[c] = s0[c];
         A.s[c] = work ? s[c] : nullptr;
         A.gs[c] = gs[c];
+        A.gend[c] = gs_end ? gs_end[c] : nullptr;
         A.ds0[c] = ds0[c];
         A.lam[c] = lam ? lam[c] : nullptr;
     }
     A.a = a;
     A.da = da;
+    A.da_acc = da_accumulate;
     A.B = shape->B;
     A.T = shape->T;
     A.D = shape->D;
@@ -1032,11 +1038,15 @@ pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
     A.records = reinterpret_cast<float *>(base + wl.records);
     A.da_part = reinterpret_cast<float *>(base + wl.da_part);
 
-    if (pl.channels == 0) {
-        // nothing per channel; da over D = 0 channels is empty as well
-        return PARARNN_OK;
-    }
     const int tpb = 256;
+    if (pl.channels == 0) {
+        // no batch rows (or no channels): da is a sum of no terms
+        if (shape->D == 0) return PARARNN_OK;
+        const int64_t n = (int64_t)G * shape->D;
+        hipLaunchKernelGGL(da_reduce_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
+                           strm, A, G);
+        return hipGetLastError() == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP;
+    }
     {
         const int64_t n = pl.units;
         hipLaunchKernelGGL(adjoint_init_kernel, dim3((unsigned)((n + tpb - 1) / tpb)), dim3(tpb), 0,
@@ -1064,3 +1074,4 @@ pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
 }
 
 }  // namespace
+

@@ -19,8 +19,9 @@ and for the backward pass, which for very long sequences dominates memory
   per chunk instead of S·B·D·T).  The backward walks the chunks from last to
   first: it re-solves the chunk from its boundary state, then runs the
   adjoint scan over the chunk with the gradient that flows into the chunk's
-  last state from the next chunk (that chunk's initial-state gradient) added
-  to the upstream gradient at the chunk's last step.  The adjoint system is
+  last state from the next chunk (that chunk's initial-state gradient) as
+  the adjoint's terminal gradient, which the kernel adds at the chunk's last
+  step; the adjoint also adds the chunk's dL/da to the running sum.  The adjoint system is
   linear and block-bidiagonal (forpes.ru, §1.3), so the chunked sweep is the
   same reverse recurrence as the one-piece adjoint, cut at chunk boundaries.
   Cost: one more forward solve per chunk.
@@ -130,8 +131,7 @@ class _Checkpointed(torch.autograd.Function):
         g_buf = [torch.empty((B, D, L), dtype=torch.float32, device=dev) for _ in range(S)]
         du = [torch.empty_strided(p.shape, p.stride(), dtype=torch.float32, device=dev)
               for p in u]
-        da = torch.zeros((G, D), dtype=torch.float32, device=dev)
-        da_k = torch.empty((G, D), dtype=torch.float32, device=dev)
+        da = torch.empty((G, D), dtype=torch.float32, device=dev)
         carry = [[torch.empty((B, D), dtype=torch.float32, device=dev) for _ in range(S)]
                  for _ in range(2)]
         have_carry = False
@@ -142,18 +142,15 @@ class _Checkpointed(torch.autograd.Function):
             s_k = [x[:, :, :n] for x in s_buf]
             _solve_span(cell, [p[:, :, t0:t1] for p in u], a, start, s_k, ctx.tol,
                         ctx.max_iters, False, None)
-            g_k = [x[:, :, :n] for x in g_buf]
-            for c in range(S):
-                if grads[c] is None:
-                    g_k[c].zero_()
-                else:
-                    g_k[c].copy_(grads[c][:, :, t0:t1])
-                if have_carry:
-                    g_k[c][:, :, n - 1] += carry[(k + 1) % 2][c]
+            g_k = [None if grads[c] is None else g_buf[c][:, :, :n].copy_(grads[c][:, :, t0:t1])
+                   for c in range(S)]
+            # the next chunk's dL/ds_0 enters at this chunk's last step, and
+            # dL/da accumulates over chunks, both inside the adjoint kernels
             pr.adjoint(cell, [p[:, :, t0:t1] for p in u], a, start, s_k, g_k,
-                       out=dict(du=[x[:, :, t0:t1] for x in du], da=da_k, ds0=carry[k % 2],
+                       gs_end=carry[(k + 1) % 2] if have_carry else None,
+                       da_accumulate=have_carry,
+                       out=dict(du=[x[:, :, t0:t1] for x in du], da=da, ds0=carry[k % 2],
                                 lam=None))
-            da += da_k
             have_carry = True
         ds0 = carry[0]
         du = [g if g.dtype == p.dtype else g.to(p.dtype) for g, p in zip(du, u)]

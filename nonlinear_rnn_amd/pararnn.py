@@ -6,8 +6,9 @@ and the current HIP stream into the pointers and sizes the ABI takes, and
 raises on a non-OK status.  There is no fallback: if the library or a GPU
 is missing, the calls raise.
 
-Names follow the ABI: ``solve_gru``, ``solve_lstm``, ``adjoint``, ``scan``,
-``workspace_bytes``, ``plan``.
+Names follow the ABI: ``solve_gru``, ``solve_lstm``,
+``adjoint``, ``scan``, ``sequential``, ``project``, ``workspace_bytes``,
+``plan``.
 """
 import ctypes
 import os
@@ -88,8 +89,8 @@ def load():
     lib.pararnn_scan.restype = i32
     lib.pararnn_scan.argtypes = [i32, P(Shape), vp, vp, vp, vp, i32, P(Newton), vp, sz, vp]
     lib.pararnn_adjoint.restype = i32
-    lib.pararnn_adjoint.argtypes = [i32, P(Shape), vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                    P(Newton), vp, sz, vp]
+    lib.pararnn_adjoint.argtypes = [i32, P(Shape), vp, i32, vp, vp, vp, vp, vp, vp, vp, i32,
+                                    vp, vp, P(Newton), vp, sz, vp]
     _lib = lib
     return lib
 
@@ -113,6 +114,112 @@ def _ptr_array(ts):
     for i, t in enumerate(ts):
         arr[i] = None if t is None else t.data_ptr()
     return arr
+
+
+# ------------------------------------------------------- argument checks ---
+# Every check runs before the library is called: a tensor of the wrong
+# dtype, shape, layout or device would otherwise hand the kernels a pointer
+# they read or write out of bounds.  Shape and dtype are checked before the
+# device, so each message names the first thing that is wrong.
+
+def _require(cond, msg):
+    """Raise ValueError(msg) if not cond; msg may be a callable, so that the
+    message is only built on failure (these checks run on every call)."""
+    if not cond:
+        raise ValueError(msg() if callable(msg) else msg)
+
+
+def _is_tensor(t):
+    return isinstance(t, torch.Tensor)
+
+
+def _plane_dims(planes, name):
+    """(B, D, T) shared by every non-None plane (indexed [B][D][T])."""
+    dims = None
+    for p in planes:
+        if p is None:
+            continue
+        if not _is_tensor(p) or p.dim() != 3:
+            raise ValueError(f"{name}: planes must be 3-d tensors [B][D][T]")
+        if dims is None:
+            dims = p.shape
+        elif p.shape != dims:
+            raise ValueError(f"{name}: every plane must have the same shape")
+    if dims is None:
+        raise ValueError(f"{name}: no planes given")
+    return tuple(dims)
+
+
+_F32_ONLY = (torch.float32,)
+_U_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _gate_planes(u, G):
+    """Checks the G projection planes (same shape [B][D][T], all float32 or
+    all bfloat16); returns ((B, D, T), ABI dtype code).  One pass, since it
+    runs on every solve."""
+    if len(u) != G:
+        raise ValueError(f"expected {G} gate planes, got {len(u)}")
+    p0 = u[0]
+    if not _is_tensor(p0) or p0.dim() != 3:
+        raise ValueError("u: planes must be 3-d tensors [B][D][T]")
+    dims, dt = p0.shape, p0.dtype
+    if dt is torch.float32:
+        code = F32
+    elif dt is torch.bfloat16:
+        code = BF16
+    else:
+        raise ValueError("u planes must be float32 or bfloat16")
+    for p in u[1:]:
+        if not _is_tensor(p) or p.shape != dims:
+            raise ValueError("u: every plane must have the same shape [B][D][T]")
+        if p.dtype is not dt:
+            raise ValueError("u planes must all be float32 or all bfloat16")
+    return tuple(dims), code
+
+
+def _check_planes(planes, name, dims, dtypes=_F32_ONLY, allow_none=False):
+    for p in planes:
+        if p is None:
+            if not allow_none:
+                raise ValueError(f"{name}: a plane is missing")
+            continue
+        if not _is_tensor(p) or p.shape != dims:
+            raise ValueError(f"{name}: planes must be [B][D][T] = {list(dims)}")
+        if p.dtype not in dtypes:
+            raise ValueError(f"{name}: planes must be {' or '.join(map(str, dtypes))}")
+
+
+def _check_dense(t, name, dims):
+    if not _is_tensor(t) or t.shape != dims:
+        raise ValueError(f"{name}: expected a tensor of shape {list(dims)}")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name}: must be float32")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _check_devices(dev, tensors):
+    """Every tensor on `dev`, and `dev` a GPU (checked last)."""
+    for name, t in tensors:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, expected {dev} (the device of u)")
+    if dev.type != "cuda":
+        raise ValueError(f"tensors are on {dev}: the kernels need GPU device memory")
+
+
+def _record_on(stream, tensors):
+    """Tensors allocated on the current stream but written on another one:
+    tell torch's allocator, so it does not hand their memory out again
+    before that stream's work is done."""
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream(stream.device)
+    if stream.cuda_stream == cur.cuda_stream:
+        return
+    for t in tensors:
+        if t is not None and t.numel():
+            t.record_stream(stream)
 
 
 def _strides(planes, name):
@@ -219,7 +326,7 @@ class Workspace:
 
 
 _ws = Workspace()
-_ws_sizes = {}  # solve workspace bytes by (cell, shape, strides, Newton options)
+_ws_sizes = {}  # (shape record, options record, workspace bytes) by solve arguments
 
 
 def _stream_handle(stream):
@@ -240,29 +347,40 @@ def _solve(cell, u, a, s0, out, tol, max_iters, steps_per_lane, waves_per_block,
            init_from_output, info, workspace, stream):
     lib = load()
     G, S = N_GATES[cell], N_STATES[cell]
-    if len(u) != G or len(s0) != S:
-        raise ValueError("wrong number of gate or state planes")
-    B, D, T = u[0].shape
+    _require(len(s0) == S, "wrong number of state planes")
+    (B, D, T), udt = _gate_planes(u, G)
+    _check_dense(a, "a", (G, D))
+    for i, x in enumerate(s0):
+        _check_dense(x, f"initial state {i}", (B, D))
     dev = u[0].device
+    allocated = []
     if out is None:
+        _require(not init_from_output, "init_from_output needs the output planes")
         out = _new_planes(S, B, T, D, _strides(u, "u"), dev)
-        if init_from_output:
-            raise ValueError("init_from_output needs the output planes")
+        allocated += out
+    out = list(out)
+    _require(len(out) == S, "wrong number of output planes")
+    _check_planes(out, "states", (B, D, T))
+    _check_devices(dev, [("u", p) for p in u] + [("a", a)] + [("initial state", x) for x in s0]
+                   + [("states", x) for x in out] + [("workspace", workspace)])
     us, ss = _strides(u, "u"), _strides(out, "states")
-    shape = make_shape(B, T, D, us, ss)
-    newton = make_newton(tol, max_iters, steps_per_lane, waves_per_block, init_from_output)
-    # the size depends on these arguments only; cached so that small solves
-    # do not pay a second library call per launch
+    # the shape and option records and the workspace size depend on these
+    # arguments only; cached so that small solves do not rebuild them (nor
+    # pay a second library call) on every launch
     wkey = (cell, B, T, D, us, ss, tol, max_iters, steps_per_lane, waves_per_block,
             bool(init_from_output))
-    nws = _ws_sizes.get(wkey)
-    if nws is None:
+    hit = _ws_sizes.get(wkey)
+    if hit is None:
         if len(_ws_sizes) >= 4096:
             _ws_sizes.clear()
-        nws = _ws_sizes[wkey] = workspace_bytes(cell, shape, newton)
+        shape = make_shape(B, T, D, us, ss)
+        newton = make_newton(tol, max_iters, steps_per_lane, waves_per_block, init_from_output)
+        hit = _ws_sizes[wkey] = (shape, newton, workspace_bytes(cell, shape, newton))
+    shape, newton, nws = hit
     ws = workspace if workspace is not None else _ws.get(nws, dev, stream)
     info_t = torch.empty(INFO_BYTES, dtype=torch.uint8, device=dev) if info else None
-    args = [ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a)]
+    _record_on(stream, allocated + [info_t])
+    args = [ctypes.byref(shape), _ptr_array(u), udt, _ptr(a)]
     args += [_ptr(x) for x in s0] + [_ptr(x) for x in out]
     args += [ctypes.byref(newton), _ptr(info_t), _ptr(ws),
              0 if ws is None else ws.numel(), _stream_handle(stream)]
@@ -299,29 +417,47 @@ def read_info(info_t) -> dict:
     return decode_info(info_t.cpu().numpy().tobytes())
 
 
-def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
-            waves_per_block=0, workspace=None, stream=None, out=None):
+def adjoint(cell, u, a, s0, s, gs, *, gs_end=None, da_accumulate=False, with_lambda=False,
+            steps_per_lane=0, waves_per_block=0, workspace=None, stream=None, out=None):
     """Backward pass of a converged solve for L = sum_t <gs_t, s_t>.
     cell "gru" (s0, s, gs: [h]) or "lstm" ([c, h]); an entry of gs may be
-    None (zero).  Returns dict(du=[G planes], da [G][D], ds0=[S], lam=[S] or
-    None), all float32 device tensors; `out`, a dict of that form returned by
-    an earlier call on the same shapes, is written in place instead of
-    allocating."""
+    None (zero).  ``gs_end`` (None, or S [B][D] tensors / None) is added to
+    dL/ds_T: the ds0 a continuation of the sequence sends back.  With
+    ``da_accumulate`` the new dL/da is added to ``out["da"]``.  Returns
+    dict(du=[G planes], da [G][D], ds0=[S], lam=[S] or None), all float32
+    device tensors; `out`, a dict of that form returned by an earlier call on
+    the same shapes, is written in place instead of allocating."""
     lib = load()
+    _require(cell in CELLS or cell in (GRU, LSTM), f"unknown cell {cell!r}")
     cell = CELLS.get(cell, cell)
     G, S = N_GATES[cell], N_STATES[cell]
     u, s0, s, gs = list(u), list(s0), list(s), list(gs)
-    if len(u) != G or len(s0) != S or len(s) != S or len(gs) != S:
-        raise ValueError("wrong number of gate or state planes")
-    B, D, T = u[0].shape
+    _require(len(u) == G and len(s0) == S and len(s) == S and len(gs) == S,
+             "wrong number of gate or state planes")
+    B, D, T = _plane_dims(u, "u")
+    _check_planes(u, "u", (B, D, T), _U_DTYPES)
+    _u_dtype(u)
+    _check_dense(a, "a", (G, D))
+    for i, x in enumerate(s0):
+        _check_dense(x, f"initial state {i}", (B, D))
+    _check_planes(s, "states", (B, D, T))
+    _check_planes(gs, "upstream gradients", (B, D, T), allow_none=True)
+    if gs_end is not None:
+        gs_end = list(gs_end)
+        _require(len(gs_end) == S, "gs_end: one [B][D] tensor (or None) per state component")
+        for i, x in enumerate(gs_end):
+            if x is not None:
+                _check_dense(x, f"gs_end[{i}]", (B, D))
+    _require(not da_accumulate or out is not None, "da_accumulate needs out['da'] to add to")
     dev = u[0].device
     us = _strides(u, "u") or (D * T, T, 1)
     ss = _strides(s + [g for g in gs if g is not None], "states") or (D * T, T, 1)
+    allocated = []
     if out is not None:
         du, da, ds0, lam = list(out["du"]), out["da"], list(out["ds0"]), out.get("lam")
         lam = list(lam) if (lam is not None and with_lambda) else None
         dense = (D * T, T, 1)
-        if (len(du) != G or len(ds0) != S or tuple(da.shape) != (G, D)
+        if (len(du) != G or len(ds0) != S or not _is_tensor(da) or tuple(da.shape) != (G, D)
                 or any(tuple(x.shape) != (B, D, T) for x in du + (lam or []))
                 or (_strides(du, "du") or dense) != us
                 or any(tuple(x.shape) != (B, D) for x in ds0)
@@ -341,13 +477,21 @@ def adjoint(cell, u, a, s0, s, gs, *, with_lambda=False, steps_per_lane=0,
         ds0 = [torch.empty((B, D), dtype=torch.float32, device=dev) for _ in range(S)]
         lam = ([torch.empty_strided((B, D, T), ss, dtype=torch.float32, device=dev)
                 for _ in range(S)] if with_lambda else None)
+        allocated = du + [da] + ds0 + (lam or [])
+    _check_devices(dev, [("u", p) for p in u] + [("a", a)]
+                   + [("initial state", x) for x in s0] + [("states", x) for x in s]
+                   + [("upstream gradient", x) for x in gs]
+                   + [("gs_end", x) for x in (gs_end or [])] + [("workspace", workspace)])
+    _record_on(stream, allocated)
     shape = make_shape(B, T, D, us, ss)
     newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
     nws = workspace_bytes(cell, shape, newton, adjoint=True)
     ws = workspace if workspace is not None else _ws.get(nws, dev, stream)
     _check(lib.pararnn_adjoint(cell, ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a),
-                               _ptr_array(s0), _ptr_array(s), _ptr_array(gs), _ptr_array(du),
-                               _ptr(da), _ptr_array(ds0),
+                               _ptr_array(s0), _ptr_array(s), _ptr_array(gs),
+                               _ptr_array(gs_end) if gs_end is not None else None,
+                               _ptr_array(du), _ptr(da), 1 if da_accumulate else 0,
+                               _ptr_array(ds0),
                                _ptr_array(lam) if lam is not None else None,
                                ctypes.byref(newton), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream_handle(stream)))
@@ -372,11 +516,15 @@ def project(x, w, bias=None, *, out=None, out_dtype=torch.float32, stream=None):
     if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (M,)
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 [M]")
+    allocated = []
     if out is None:
         out = torch.empty((B, M, T), dtype=out_dtype, device=x.device)
+        allocated = [out]
     if tuple(out.shape) != (B, M, T) or out.dtype not in (torch.float32, torch.bfloat16) or (
             out.numel() and out.stride(2) != 1):
         raise ValueError("out must be [B][M][T] float32 or bfloat16, time contiguous")
+    _check_devices(x.device, [("w", w), ("bias", bias), ("out", out)])
+    _record_on(stream, allocated)
     # strides of size-1 dimensions are arbitrary in torch: use dense ones
     xst = x.stride(1) if T > 1 else I
     usm = out.stride(1) if M > 1 else T
@@ -393,24 +541,30 @@ def sequential(cell, u, a, s0, *, out=None, stream=None):
     (no Newton iteration).  cell "gru" (s0: [h0]) or "lstm" ([c0, h0]); u as
     for the solves.  Returns the S state planes [B][D][T] (float32)."""
     lib = load()
+    _require(cell in CELLS or cell in (GRU, LSTM), f"unknown cell {cell!r}")
     cell = CELLS.get(cell, cell)
     G, S = N_GATES[cell], N_STATES[cell]
     u, s0 = list(u), list(s0)
-    if len(u) != G or len(s0) != S:
-        raise ValueError("wrong number of gate or state planes")
-    B, D, T = u[0].shape
+    _require(len(u) == G and len(s0) == S, "wrong number of gate or state planes")
+    B, D, T = _plane_dims(u, "u")
+    _check_planes(u, "u", (B, D, T), _U_DTYPES)
+    _u_dtype(u)
+    _check_dense(a, "a", (G, D))
+    for i, x in enumerate(s0):
+        _check_dense(x, f"initial state {i}", (B, D))
     dev = u[0].device
     us = _strides(u, "u") or (D * T, T, 1)
+    allocated = []
     if out is None:
         out = _new_planes(S, B, T, D, us, dev)
+        allocated = out
     out = list(out)
-    if len(out) != S or any(tuple(x.shape) != (B, D, T) or x.dtype != torch.float32
-                            for x in out):
-        raise ValueError("out must be S float32 planes [B][D][T]")
+    _require(len(out) == S, "out must be S float32 planes [B][D][T]")
+    _check_planes(out, "out", (B, D, T))
     ss = _strides(out, "states") or (D * T, T, 1)
-    for x in s0:
-        if tuple(x.shape) != (B, D) or not x.is_contiguous() or x.dtype != torch.float32:
-            raise ValueError("initial states must be contiguous float32 [B][D]")
+    _check_devices(dev, [("u", p) for p in u] + [("a", a)]
+                   + [("initial state", x) for x in s0] + [("out", x) for x in out])
+    _record_on(stream, allocated)
     shape = make_shape(B, T, D, us, ss)
     _check(lib.pararnn_sequential(cell, ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a),
                                   _ptr_array(s0), _ptr_array(out), _stream_handle(stream)))
@@ -426,14 +580,28 @@ def scan(A, b, x0=None, *, reverse=False, out=None, steps_per_lane=0, waves_per_
     lib = load()
     A, b = list(A), list(b)
     S = len(b)
-    if S not in (1, 2) or len(A) != S * S:
-        raise ValueError("state size must be 1 or 2 (A has S*S planes, b has S)")
-    B, D, T = b[0].shape
+    _require(S in (1, 2) and len(A) == S * S,
+             "state size must be 1 or 2 (A has S*S planes, b has S)")
+    B, D, T = _plane_dims(A + b, "A/b")
+    _check_planes(A + b, "A/b", (B, D, T))
+    if x0 is not None:
+        x0 = list(x0)
+        _require(len(x0) == S, "x0: one [B][D] plane per state component")
+        for i, x in enumerate(x0):
+            _check_dense(x, f"x0[{i}]", (B, D))
     dev = b[0].device
     ins = _strides(A + b, "A/b") or (D * T, T, 1)
+    allocated = []
     if out is None:
         out = _new_planes(S, B, T, D, ins, dev)
+        allocated = out
+    out = list(out)
+    _require(len(out) == S, "out: one plane per state component")
+    _check_planes(out, "x", (B, D, T))
     outs = _strides(out, "x") or (D * T, T, 1)
+    _check_devices(dev, [("A/b", p) for p in A + b] + [("x0", x) for x in (x0 or [])]
+                   + [("x", x) for x in out] + [("workspace", workspace)])
+    _record_on(stream, allocated)
     shape = make_shape(B, T, D, ins, outs)
     newton = make_newton(0.0, 0, steps_per_lane, waves_per_block)
     nws = int(lib.pararnn_scan_workspace_bytes(S, ctypes.byref(shape), ctypes.byref(newton)))

@@ -240,8 +240,8 @@ void gru_adjoint_case(int64_t B, int64_t T, int64_t D, uint64_t seed)
     const float *s0[1] = {dh0d.f()}, *s[1] = {dh.f()}, *gs[1] = {dg.f()};
     float *duo[3] = {gu[0].f(), gu[1].f(), gu[2].f()}, *ds0[1] = {gdh0.f()};
     const pararnn_status_t st = pararnn_adjoint(PARARNN_GRU, &sh, uu, PARARNN_F32, da.f(), s0,
-                                                s, gs, duo, gda.f(), ds0, nullptr, nullptr,
-                                                ws.p, wsb, nullptr);
+                                                s, gs, nullptr, duo, gda.f(), 0, ds0, nullptr,
+                                                nullptr, ws.p, wsb, nullptr);
     if (st != PARARNN_OK) {
         std::printf("pararnn_adjoint: %s\n", pararnn_status_string(st));
         ++failures;

@@ -221,12 +221,15 @@ def test_lstm_and_adjoint_reject_bad_arguments():
     assert lib.pararnn_solve_lstm(ctypes.byref(shape), u, 5, 1, 1, 1, 1, 1,
                                   ctypes.byref(n), None, None, 0, None) == 2
     s2 = (ctypes.c_void_p * 2)(1, 1)
-    assert lib.pararnn_adjoint(3, ctypes.byref(shape), u, 0, 1, s2, s2, s2, u, 1, s2, None,
-                               None, None, 0, None) == 1
-    assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, 1, s2, s2, s2, u, 1, s2, None,
-                               None, None, 0, None) == 3
-    assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, None, s2, s2, s2, u, 1, s2, None,
-                               None, None, 0, None) == 1
+    assert lib.pararnn_adjoint(3, ctypes.byref(shape), u, 0, 1, s2, s2, s2, None, u, 1, 0, s2,
+                               None, None, None, 0, None) == 1
+    assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, 1, s2, s2, s2, None, u, 1, 0, s2,
+                               None, None, None, 0, None) == 3
+    assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, None, s2, s2, s2, None, u, 1, 0, s2,
+                               None, None, None, 0, None) == 1
+    # da_accumulate is a 0/1 flag
+    assert lib.pararnn_adjoint(1, ctypes.byref(shape), u, 0, 1, s2, s2, s2, s2, u, 1, 2, s2,
+                               None, None, None, 0, None) == 1
 
 
 def test_sequential_rejects_bad_arguments_before_any_device_call():
@@ -306,3 +309,69 @@ def test_kernel_digest_ignores_comments_and_layout():
     b = bench._code_only("/* doc */\nint f(int x) {\n\n  return x + 1;\n}")
     assert a == b
     assert a != bench._code_only("int f(int x) { return x + 2; }")
+
+
+def test_binding_rejects_bad_tensors_before_any_call():
+    """The binding checks dtype, shape, layout and device of every tensor
+    before calling the library (a float64 output or a 1-d weight vector
+    would otherwise be written or read out of bounds by the kernels).  Here,
+    on the CPU, every case must raise ValueError; the last one reaches the
+    device check, since CPU memory is not device memory."""
+    import torch
+
+    B, D, T = 2, 3, 16
+    f32 = dict(dtype=torch.float32)
+
+    def planes(n, shape=(B, D, T), **kw):
+        return [torch.zeros(shape, **(kw or f32)) for _ in range(n)]
+
+    u, a, h0 = planes(3), torch.zeros(3, D), torch.zeros(B, D)
+    out = torch.zeros(B, D, T)
+    bad = [
+        dict(u=planes(2)),                                          # gate count
+        dict(u=planes(2) + [torch.zeros(B, D, T + 1)]),             # unequal planes
+        dict(u=[torch.zeros(B * D * T)] * 3),                       # not [B][D][T]
+        dict(u=planes(3, dtype=torch.float64)),                     # dtype
+        dict(u=planes(2) + planes(1, dtype=torch.bfloat16)),        # mixed dtypes
+        dict(a=torch.zeros(3 * D)),                                 # 1-d weights
+        dict(a=torch.zeros(D, 3).t()),                              # non-contiguous
+        dict(a=torch.zeros(3, D, dtype=torch.float64)),
+        dict(h0=torch.zeros(D, B).t()),                             # transposed h0
+        dict(h0=torch.zeros(B + 1, D)),
+        dict(out=torch.zeros(B, D, T, dtype=torch.bfloat16)),       # output dtype
+        dict(out=torch.zeros(B, D, T, dtype=torch.float64)),
+        dict(out=torch.zeros(B, D, T - 1)),
+        dict(),                                                     # CPU tensors
+    ]
+    for case in bad:
+        kw = dict(u=u, a=a, h0=h0, out=out)
+        kw.update(case)
+        with pytest.raises(ValueError):
+            pr.solve_gru(kw["u"], kw["a"], kw["h0"], out=kw["out"])
+    with pytest.raises(ValueError):
+        pr.solve_lstm(planes(4), torch.zeros(4, D), h0, torch.zeros(B, D, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        pr.solve_gru(u, a, h0, init_from_output=True)
+    # adjoint: states, upstream gradients, weights
+    s, g = planes(1), planes(1)
+    for case in [dict(s=planes(1, shape=(B, D, T - 1))), dict(gs=planes(1, dtype=torch.float64)),
+                 dict(a=torch.zeros(3, D + 1)), dict(s0=[torch.zeros(B, D, 1)]), dict()]:
+        kw = dict(u=u, a=a, s0=[h0], s=s, gs=g)
+        kw.update(case)
+        with pytest.raises(ValueError):
+            pr.adjoint("gru", kw["u"], kw["a"], kw["s0"], kw["s"], kw["gs"])
+    with pytest.raises(ValueError):
+        pr.adjoint("tanh", u, a, [h0], s, g)
+    # sequential and scan
+    for case in [dict(a=torch.zeros(2, D)), dict(out=planes(1, dtype=torch.float64)), dict()]:
+        kw = dict(a=a, out=planes(1))
+        kw.update(case)
+        with pytest.raises(ValueError):
+            pr.sequential("gru", u, kw["a"], [h0], out=kw["out"])
+    for case in [dict(A=planes(2)), dict(b=planes(1, dtype=torch.float64)),
+                 dict(x0=[torch.zeros(B, D + 1)]), dict()]:
+        kw = dict(A=planes(1), b=planes(1), x0=None)
+        kw.update(case)
+        with pytest.raises(ValueError):
+            pr.scan(kw["A"], kw["b"], kw["x0"])
+
