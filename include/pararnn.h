@@ -73,7 +73,8 @@ typedef enum {
     PARARNN_ERR_INVALID = 1,     /* null pointer, size < 0, bad stride      */
     PARARNN_ERR_UNSUPPORTED = 2, /* valid request this build does not serve */
     PARARNN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than needed   */
-    PARARNN_ERR_HIP = 4          /* the HIP runtime reported a launch error */
+    PARARNN_ERR_HIP = 4,         /* the HIP runtime reported a launch error */
+    PARARNN_ERR_SCRATCH = 5      /* needs more than the static scratch      */
 } pararnn_status_t;
 
 typedef enum { PARARNN_F32 = 0, PARARNN_BF16 = 1 } pararnn_dtype_t;
@@ -267,6 +268,32 @@ typedef struct {
 pararnn_status_t pararnn_project(const pararnn_proj_shape_t *shape, const void *x,
                                  const void *w, const float *bias, void *u,
                                  pararnn_dtype_t u_dtype, void *stream);
+
+/*
+ * pararnn_solve_gru without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, results and errors are those
+ * of pararnn_solve_gru; the workspace (time-block hand-off, convergence
+ * records of the info record, staging of planes that are not
+ * time-contiguous when it fits) comes from an array inside the library of
+ * PARARNN_STATIC_SCRATCH_BYTES per GPU, held from the first call on that GPU
+ * until the process ends.  A problem that needs more returns
+ * PARARNN_ERR_SCRATCH before any HIP call (planes that are not
+ * time-contiguous and do not fit are read step by step instead of staged).
+ * The call allocates nothing and frees nothing; the first call on a device
+ * looks up the array's device address (the caller's stream must belong to
+ * the current device, else PARARNN_ERR_INVALID).  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind (the solve clears
+ * what must start at zero with a kernel): calls whose executions overlap on
+ * one GPU (different streams, concurrent graph replays) race and must be
+ * serialised by the caller.
+ */
+#define PARARNN_STATIC_SCRATCH_BYTES (32u << 20)
+pararnn_status_t pararnn_solve_gru_noalloc(const pararnn_shape_t *shape, const void *const u[3],
+                                           pararnn_dtype_t u_dtype, const float *a,
+                                           const float *h0, float *h,
+                                           const pararnn_newton_t *opt, pararnn_info_t *info,
+                                           void *stream);
 
 /* Static description of a status code. */
 const char *pararnn_status_string(pararnn_status_t status);

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <utility>
 
 #define PARARNN_DEFINE_AUX_KERNELS
@@ -808,6 +809,9 @@ const char *pararnn_status_string(pararnn_status_t s)
     case PARARNN_ERR_UNSUPPORTED: return "unsupported argument combination";
     case PARARNN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PARARNN_ERR_HIP: return "HIP runtime error at launch";
+    case PARARNN_ERR_SCRATCH:
+        return "problem needs more scratch than the library's static array "
+               "(PARARNN_STATIC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -1075,3 +1079,72 @@ pararnn_status_t adjoint_core(pararnn_cell_t cell, const pararnn_shape_t *shape,
 
 }  // namespace
 
+// ------------------------------------------------ static scratch solve ---
+// For callers that cannot allocate device memory: the workspace of
+// pararnn_solve_gru_noalloc is this file-scope array.  Every GPU the library
+// runs on holds its own copy (at its own address) until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory, so
+// the device address is looked up once per device with hipGetSymbolAddress
+// and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[PARARNN_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array; looked up on the first
+// call on a device (with that device current, which is the device of the
+// caller's stream) and kept.
+pararnn_status_t device_scratch(void *stream, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PARARNN_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+            return PARARNN_ERR_HIP;
+        if (sdev != dev) return PARARNN_ERR_INVALID;  // the stream's device must be current
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return PARARNN_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PARARNN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pararnn_status_t pararnn_solve_gru_noalloc(const pararnn_shape_t *shape, const void *const u[3],
+                                           pararnn_dtype_t u_dtype, const float *a,
+                                           const float *h0, float *h,
+                                           const pararnn_newton_t *opt, pararnn_info_t *info,
+                                           void *stream)
+{
+    // every size check before any HIP call: what the solve needs beyond
+    // its inputs and outputs must fit the static array
+    pararnn_status_t st = check_newton(opt);
+    if (st != PARARNN_OK) return st;
+    Plan pl;
+    st = make_plan(PARARNN_GRU, shape, opt, 0, pl);
+    if (st != PARARNN_OK) return st;
+    const SolveWs wl = solve_ws_layout(PARARNN_GRU, pl, opt);
+    const size_t need = info ? wl.total : wl.multi;
+    if (need > (size_t)PARARNN_STATIC_SCRATCH_BYTES) return PARARNN_ERR_SCRATCH;
+    void *ws = nullptr;
+    st = device_scratch(stream, &ws);
+    if (st != PARARNN_OK) return st;
+    // planes that are not time-contiguous are staged through the scratch
+    // when they fit there and gathered step by step otherwise
+    return pararnn_solve_gru(shape, u, u_dtype, a, h0, h, opt, info, ws,
+                             (size_t)PARARNN_STATIC_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"

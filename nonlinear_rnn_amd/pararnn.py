@@ -6,7 +6,7 @@ and the current HIP stream into the pointers and sizes the ABI takes, and
 raises on a non-OK status.  There is no fallback: if the library or a GPU
 is missing, the calls raise.
 
-Names follow the ABI: ``solve_gru``, ``solve_lstm``,
+Names follow the ABI: ``solve_gru``, ``solve_gru_noalloc``, ``solve_lstm``,
 ``adjoint``, ``scan``, ``sequential``, ``project``, ``workspace_bytes``,
 ``plan``.
 """
@@ -53,6 +53,7 @@ class Newton(ctypes.Structure):
 
 
 INFO_BYTES = 32
+STATIC_SCRATCH_BYTES = 32 << 20  # PARARNN_STATIC_SCRATCH_BYTES
 _INFO_FMT = "<iifiqq"
 
 _lib = None
@@ -77,6 +78,8 @@ def load():
                                  P(ctypes.c_int32), P(ctypes.c_int64)]
     lib.pararnn_solve_gru.restype = i32
     lib.pararnn_solve_gru.argtypes = [P(Shape), vp, i32, vp, vp, vp, P(Newton), vp, vp, sz, vp]
+    lib.pararnn_solve_gru_noalloc.restype = i32
+    lib.pararnn_solve_gru_noalloc.argtypes = [P(Shape), vp, i32, vp, vp, vp, P(Newton), vp, vp]
     lib.pararnn_solve_lstm.restype = i32
     lib.pararnn_solve_lstm.argtypes = [P(Shape), vp, i32, vp, vp, vp, vp, vp, P(Newton), vp,
                                        vp, sz, vp]
@@ -400,6 +403,37 @@ def solve_gru(u, a, h0, *, out=None, tol=1e-6, max_iters=20, steps_per_lane=0,
     s, info_t = _solve(GRU, list(u), a, [h0], out, tol, max_iters, steps_per_lane,
                        waves_per_block, init_from_output, info, workspace, stream)
     return s[0], info_t
+
+
+def solve_gru_noalloc(u, a, h0, out, *, tol=1e-6, max_iters=20, steps_per_lane=0,
+                      waves_per_block=0, init_from_output=False, info=None, stream=None):
+    """ParaGRU Newton solve that allocates nothing: ``out`` ([B][D][T]
+    float32) and ``info`` (a 32-byte device buffer, or None) are the
+    caller's, and the library's static per-GPU scratch array serves as the
+    workspace (problems needing more than PARARNN_STATIC_SCRATCH_BYTES
+    raise).  Calls whose executions overlap on one GPU share that array
+    and must not overlap.  Returns ``out``."""
+    lib = load()
+    B, D, T = _plane_dims(list(u), "u")
+    _require(len(u) == 3, "wrong number of gate planes")
+    _check_planes(u, "u", (B, D, T), _U_DTYPES)
+    _u_dtype(u)
+    _check_dense(a, "a", (3, D))
+    _check_dense(h0, "initial state", (B, D))
+    _check_planes([out], "states", (B, D, T))
+    if info is not None:
+        _require(_is_tensor(info) and info.dtype == torch.uint8 and info.numel() == INFO_BYTES
+                 and info.is_contiguous(), f"info must be a contiguous {INFO_BYTES}-byte uint8 buffer")
+    dev = u[0].device
+    _check_devices(dev, [("u", p) for p in u] + [("a", a), ("initial state", h0), ("states", out),
+                         ("info", info)])
+    us, ss = _strides(u, "u"), _strides([out], "states")
+    shape = make_shape(B, T, D, us, ss)
+    newton = make_newton(tol, max_iters, steps_per_lane, waves_per_block, init_from_output)
+    _check(lib.pararnn_solve_gru_noalloc(ctypes.byref(shape), _ptr_array(u), _u_dtype(u), _ptr(a),
+                                         _ptr(h0), _ptr(out), ctypes.byref(newton), _ptr(info),
+                                         _stream_handle(stream)))
+    return out
 
 
 def solve_lstm(u, a, c0, h0, *, out=None, tol=1e-6, max_iters=20, steps_per_lane=0,

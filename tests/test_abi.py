@@ -50,8 +50,9 @@ def test_library_exports_no_undeclared_c_functions():
 
 def test_status_strings():
     assert pr.status_string(0) == "ok"
-    for s in range(1, 5):
+    for s in range(1, 6):
         assert pr.status_string(s) != "ok"
+    assert "static" in pr.status_string(5)
     assert "unknown" in pr.status_string(99)
 
 
@@ -375,3 +376,27 @@ def test_binding_rejects_bad_tensors_before_any_call():
         with pytest.raises(ValueError):
             pr.scan(kw["A"], kw["b"], kw["x0"])
 
+
+def test_static_scratch_solve_rejects_oversized_problems_before_any_device_call():
+    """The allocation-free solve sizes its workspace on the host: a problem
+    whose time-block records exceed the static array returns
+    PARARNN_ERR_SCRATCH (5) before any HIP call, and so do bad arguments."""
+    lib = pr.load()
+    hdr = open(HEADER).read()
+    assert re.search(r"#define PARARNN_STATIC_SCRATCH_BYTES \(32u << 20\)", hdr)
+    assert pr.STATIC_SCRATCH_BYTES == 32 << 20
+    one = ctypes.c_void_p(256)
+    u = (ctypes.c_void_p * 3)(one, one, one)
+    # 1024 channels x 1024 time blocks of 64 steps, 21 records each: 336 MB
+    big = pr.make_shape(1, 65536, 1024)
+    n = pr.make_newton(1e-6, 20, steps_per_lane=1, waves_per_block=1)
+    assert pr.workspace_bytes("gru", big, n) > pr.STATIC_SCRATCH_BYTES
+    assert lib.pararnn_solve_gru_noalloc(ctypes.byref(big), u, 0, one, one, one, ctypes.byref(n),
+                                         None, None) == 5
+    assert lib.pararnn_solve_gru_noalloc(None, u, 0, one, one, one, ctypes.byref(n),
+                                         None, None) == 1
+    assert lib.pararnn_solve_gru_noalloc(ctypes.byref(big), u, 0, one, one, one, None,
+                                         None, None) == 1
+    bad = pr.make_newton(1e-6, 20, steps_per_lane=3)
+    assert lib.pararnn_solve_gru_noalloc(ctypes.byref(big), u, 0, one, one, one,
+                                         ctypes.byref(bad), None, None) == 2
