@@ -328,6 +328,55 @@ __device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_
     pred_stopped = (p == k);
 }
 
+// Carries of every iteration at once, for a time block whose predecessors
+// have all stopped before it starts (the common case: tickets hand out a
+// channel's blocks a group apart, so rank r-1 is usually done when rank r
+// begins).  Their stop iterations j_p and their per-iteration records are
+// then final, and the carry into block k at iteration q is the fold over
+// p = 0..k-1 of block p's aggregate map at q, restarted from zero at every
+// block stopped by q (a stopped block's carry-out is zero): the same carry
+// look_back() returns at q.  Lane q holds the carry of iteration q, so the
+// Newton loop reads it with readlane instead of one round trip to the
+// predecessors' records per iteration.  Returns false (nothing loaded) when
+// a predecessor is still running, when there are more than kPreloadBlocks
+// predecessors, or when iterations would not fit one lane each.
+constexpr int32_t kPreloadBlocks = 8;
+
+template <class M, class V>
+__device__ __forceinline__ bool preload_carries(const SolveArgs &A, int64_t ch, int32_t k,
+                                                V &carry, int32_t &j_last)
+{
+    constexpr int RF = MapRec<M>::kFloats;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (k > kPreloadBlocks || A.cap >= kWave) return false;
+    const int32_t *flags = A.flags + ch * A.nb;
+    const int32_t v = lane < k ? load_flag(flags + lane) : kStopBase;
+    if (!__all(v >= kStopBase)) return false;
+    after_flag();
+    const int64_t rstride = (int64_t)(A.cap + 1) * RF;
+    const float *rec = A.records + (ch * A.nb) * rstride;
+    V c = vzero<V>();
+    for (int32_t p = 0; p < k; ++p) {
+        const int32_t jp = __builtin_amdgcn_readlane(v, p) - kStopBase;
+        if (jp <= lane) {
+            c = vzero<V>();
+        } else {
+            M m;
+            rec_load(rec + p * rstride + lane * RF, m);
+            c = apply(m, c);
+        }
+    }
+    carry = c;
+    j_last = __builtin_amdgcn_readlane(v, k - 1) - kStopBase;
+    return true;
+}
+
+__device__ __forceinline__ Vec1 readlane_vec(const Vec1 &v, int src) { return {readlane_f(v.x, src)}; }
+__device__ __forceinline__ Vec2 readlane_vec(const Vec2 &v, int src)
+{
+    return {readlane_f(v.x0, src), readlane_f(v.x1, src)};
+}
+
 template <class M>
 struct Slot {
     M agg;
@@ -418,6 +467,18 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     int32_t lb_known = 0;      // this lane's predecessor's stop flag, once seen
     V din_probe = vzero<V>();
     bool stopped_probe = true;
+    // every predecessor already done: all iterations' carries in one load
+    V pre_carry = vzero<V>();
+    int32_t pre_jlast = 0;
+    const bool pre = multi && k > 0 && preload_carries<M, V>(A, ch, k, pre_carry, pre_jlast);
+    const auto carry_at = [&](int32_t i, V &din, bool &stopped) {
+        if (pre && i < kWave) {
+            din = readlane_vec(pre_carry, i);
+            stopped = pre_jlast <= i;
+        } else {
+            look_back<M, V>(A, ch, k, i, din, stopped, lb_known);
+        }
+    };
     bool ronly = false;  // this evaluation is the predicted last one
     int xp = 0;          // LDS exchange slot parity (alternates every exchange)
     for (;; ++it) {
@@ -448,7 +509,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             if (it == A.cap) break;
             if (bmx < tolb) {
                 if (!multi) break;
-                if (k > 0) look_back<M, V>(A, ch, k, it, din_probe, stopped_probe, lb_known);
+                if (k > 0) carry_at(it, din_probe, stopped_probe);
                 if (k == 0 || stopped_probe) {
                     if (threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
                     break;
@@ -510,8 +571,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         if (at_cap) break;
         V din = carry_known ? din_probe : vzero<V>();
         bool pred_stopped = carry_known ? stopped_probe : true;
-        if (multi && k > 0 && !carry_known)
-            look_back<M, V>(A, ch, k, it, din, pred_stopped, lb_known);
+        if (multi && k > 0 && !carry_known) carry_at(it, din, pred_stopped);
         carry_known = false;
         if (cbit && pred_stopped) {
             if (multi && threadIdx.x == 0) publish_flag(A.flags + unit, kStopBase + it);
