@@ -114,14 +114,12 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
         }
         if (K == 0) K = tab[pick][0];
         if (W == 0) W = tab[pick][1];
-        // Past 4096 steps a ParaGRU channel takes 8-wave time blocks of 8192
-        // steps: half the cross-block exchanges per step of 4096-step blocks,
-        // still 4 waves per SIMD (106 VGPRs, 61 KB LDS per workgroup).
-        if (kind == 0 && cell == PARARNN_GRU && opt_k_w_unset(opt) &&
-            sh->T > (int64_t)kWave * tab[0][0] * tab[0][1]) {
-            K = 16;
-            W = 8;
-        }
+        // Past 4096 steps a channel takes time blocks of 4096 steps (K = 16,
+        // W = 4): a block whose predecessors are done loads all their carries
+        // at once, so more, smaller blocks cost little and hide each other's
+        // loads better (ParaGRU bf16-u B=4 T=16384 D=4096: 4 blocks of 4096
+        // steps 1.36 ms, 2 blocks of 8192 steps 1.46 ms, 8 blocks of 2048
+        // steps 1.61 ms).
         // Few channels in one block each: spread every channel over more
         // waves at the same capacity (half the steps per lane, twice the
         // waves) until the solve has about two waves per CU.  Each lane's

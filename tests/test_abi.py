@@ -59,7 +59,7 @@ def test_status_strings():
 def test_plan_defaults():
     # one workgroup per channel up to 4096 steps, then time blocks
     assert pr.plan("gru", pr.make_shape(8, 4096, 1024)) == (16, 4, 1)
-    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (16, 8, 2)
+    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (16, 4, 4)
     # few channels: each spread over more waves at the same capacity
     assert pr.plan("gru", pr.make_shape(1, 1024, 64)) == (4, 4, 1)
     assert pr.plan("gru", pr.make_shape(1, 4096, 64)) == (8, 8, 1)

@@ -240,8 +240,8 @@ def test_many_channels(cell, dtype, T, KW):
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 def test_long_sequence_default_tiling(cell):
-    """Past 4096 steps: the default time blocks (ParaGRU 8192 steps, ParaLSTM
-    4096), a ragged last block, bf16 and float32 projections."""
+    """Past 4096 steps: the default time blocks of 4096 steps, a ragged last
+    block, bf16 and float32 projections."""
     from nonlinear_rnn_amd import pararnn as pr
     T = 17001
     K, W, nb = pr.plan(cell, pr.make_shape(2, T, 2))
