@@ -31,18 +31,23 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-# Unpacked fp32 VALU issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-ops/s
-# (the 157.3 TFLOP/s figure counts an FMA as two flops and packed fp32 as two
-# lanes; these kernels issue no packed fp32).
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-
-# Algorithmic VALU issue slots per hidden-state element and Newton pass, from
-# the cell formulas: gate pre-activations, exp2/rcp gates (a transcendental
-# issues in two slots), residual, local Jacobian, one map composition, the
-# update and the residual max.  The last pass of a unit only evaluates the
-# residual.  ParaGRU: 26 ops + 6 transcendentals per update pass, 12 + 6 on
-# the final pass; ParaLSTM (2x2 maps): 52 + 10, and 18 + 10.
-VALU_SLOTS = {"gru": (26 + 2 * 6, 12 + 2 * 6), "lstm": (52 + 2 * 10, 18 + 2 * 10)}
+# The second roof: VALU issue.  On gfx950 a plain fp32 wave64 instruction
+# (FMA, mul, add, max) occupies a SIMD for 2 cycles (32 lanes per clock:
+# 256 CUs x 4 SIMDs x 32 lanes x 2 flops x 2.4 GHz is the published
+# 157.3 TFLOP/s fp32 vector peak) and a transcendental (v_exp_f32,
+# v_rcp_f32) for 8, a quarter of that rate; a probe of independent chains
+# at 8 waves per SIMD measures 2.45 and 8.3 cycles, and exp interleaved
+# with FMAs costs the sum of both (no overlap).  These kernels issue no
+# packed fp32.
+CYC_PLAIN, CYC_TRANS = 2.0, 8.0
+SIMD_CYCLES_PER_S = 256 * 4 * 2.4e9
+# Algorithmic operations per hidden-state element and Newton pass, from the
+# cell formulas: gate pre-activations, exp2/rcp gates, residual, local
+# Jacobian, one map composition, the update and the residual max, as
+# (plain ops, transcendentals); a unit's last pass only evaluates the
+# residual.  ParaGRU: 26 + 6 per update pass, 12 + 6 on the final one;
+# ParaLSTM (2x2 maps): 52 + 10, and 18 + 10.
+VALU_OPS = {"gru": ((26, 6), (12, 6)), "lstm": ((52, 10), (18, 10))}
 HEADLINE = "gru_bf16_long"  # the largest workload
 METRIC = "hidden-state elems/sec per Newton solve (B·T·D) + % of MI355X HBM peak"
 
@@ -88,7 +93,8 @@ def _code_only(text):
 
 def kernel_source_digest(family="solve"):
     """Hash of the code a kernel family is built from: "project" (the
-    projection kernels and the ABI) or "solve" (everything else)."""
+    projection kernels and the ABI) or "solve" (everything else), plus the
+    ABI header and the build script."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nonlinear_rnn_amd", "csrc")
     names = sorted(os.listdir(csrc))
@@ -96,7 +102,10 @@ def kernel_source_digest(family="solve"):
         names = [n for n in names if n in PROJECTION_ONLY or n == "pararnn.hip"]
     else:
         names = [n for n in names if n not in PROJECTION_ONLY]
-    paths = [os.path.join(csrc, n) for n in names] + [os.path.join(ROOT, "include", "pararnn.h")]
+    # the build script carries the compile flags (and per-unit scheduler choice)
+    paths = [os.path.join(csrc, n) for n in names] + [os.path.join(ROOT, "include", "pararnn.h"),
+                                                      os.path.join(ROOT, "nonlinear_rnn_amd",
+                                                                   "build.py")]
     for path in paths:
         with open(path, encoding="utf-8") as f:
             h.update((os.path.basename(path) + _code_only(f.read())).encode())
@@ -521,14 +530,17 @@ def measure_solve(w, key, args, flush_buf, headline):
                 "hbm_frac": nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
     kernels = [kernel_stats(0, "newton_kernel", algorithmic_bytes(w))]
-    # VALU issue slots of the solve: every unit runs its updates plus one
+    # VALU issue cycles of the solve: every unit runs its updates plus one
     # final residual pass (iters_mean = updates per unit)
-    upd, fin = VALU_SLOTS[w.cell]
-    ops = w.N * (info["iters_mean"] * upd + fin)
-    tops = ops / (kernels[0]["ms_avg"] * 1e-3) / 1e12
-    kernels[0]["valu"] = {"achieved": tops, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
-                          "frac": tops / VALU_PEAK_TOPS, "ops_per_launch": ops,
-                          "ops": "algorithmic VALU lane-op issue slots (exp2/rcp = 2)"}
+    (pu, tu), (pf, tf) = VALU_OPS[w.cell]
+    n = info["iters_mean"]
+    cyc_per_elem = (n * (pu * CYC_PLAIN + tu * CYC_TRANS) + pf * CYC_PLAIN + tf * CYC_TRANS) / 64
+    t_alu_ms = w.N * cyc_per_elem / SIMD_CYCLES_PER_S * 1e3
+    kernels[0]["valu"] = {"bound": "alu", "min_ms": t_alu_ms,
+                          "frac": t_alu_ms / kernels[0]["ms_avg"],
+                          "simd_cycles_per_elem": cyc_per_elem,
+                          "ops": "algorithmic wave64 VALU issue cycles per SIMD (plain fp32 op 2, "
+                                 "exp/rcp 8) over 1024 SIMDs at 2.4 GHz"}
     if w.adjoint:
         kernels.append(kernel_stats(1, "adjoint_kernel", adjoint_bytes(w)))
     K, W, nb = pr.plan(w.cell, pr.make_shape(w.B, w.T, w.D))
