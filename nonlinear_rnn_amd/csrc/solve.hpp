@@ -506,7 +506,11 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 #pragma unroll
             for (int j = 1; j < W; ++j) bmx = max(bmx, sm.slots[xp][j].mx);
             xp ^= 1;
-            if (it == A.cap) break;
+            if (it == A.cap) {
+                // records 0..cap-1 are stored (one per full pass)
+                if (multi && threadIdx.x == 0) publish_flag(A.flags + unit, it);
+                break;
+            }
             if (bmx < tolb) {
                 if (!multi) break;
                 if (k > 0) carry_at(it, din_probe, stopped_probe);
@@ -564,9 +568,19 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         }
         const uint32_t cbit = bmx < tolb ? 1u : 0u;
         const bool at_cap = (it == A.cap);
+        // The flag that certifies a record is published one full pass later:
+        // flag `it` (records 0..it-1 complete) goes out just before record
+        // `it` is stored, when the stores of record it-1, issued a pass ago,
+        // have long completed, so the wait in publish_flag costs nothing
+        // (waiting for the record just stored stalled this wave for a store
+        // round trip every pass).  A successor still looking back per
+        // iteration sees each record one pass later; one that preloads its
+        // carries only reads the final stop flag.  Every path out of the
+        // loop publishes a flag covering every stored record.
         if (multi && threadIdx.x == 0) {
+            if (it > 0) publish_flag(A.flags + unit, it);
             rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
-            publish_flag(A.flags + unit, it + 1);
+            if (at_cap) publish_flag(A.flags + unit, it + 1);
         }
         if (at_cap) break;
         V din = carry_known ? din_probe : vzero<V>();

@@ -251,3 +251,27 @@ def test_long_sequence_default_tiling(cell):
         got, info = gpu_solve(inp, 1e-6, 30)
         assert info["converged"] and info["units"] == 4 * nb
         assert max_err(got, oracle_states(inp, rounded=True)) < TOL32
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("cap", [2, 3, 4])
+def test_time_blocks_stop_at_cap_after_a_guessed_last_pass(cell, cap):
+    """Time blocks that reach the iteration cap on a residual-only pass (the
+    guessed last evaluation: tol < max|r| < sqrt(tol)) still certify every
+    record they stored, so successors reading carries iteration by iteration
+    finish; the iterate is the oracle's DEER iterate after `cap` updates
+    (blocks that stop earlier differ from it by less than tol)."""
+    from nonlinear_rnn_amd import pararnn as pr
+    T, D = 3000, 4
+    inp = make_inputs(cell, 1, T, D, 900 + cap, s0_std=0.3, f_bias=1.0)
+    K, W, nb = pr.plan(cell, pr.make_shape(1, T, D), pr.make_newton(1e-6, cap, 4, 1))
+    assert nb == 12
+    got, info = gpu_solve(inp, 1e-6, cap, 4, 1)
+    assert info["iters"] == cap and info["units"] == D * nb
+    u = deer.from_planes(inp.u)
+    a = deer.a_per_channel(inp.a, 1)
+    s0 = np.stack([p.reshape(-1).astype(np.float64) for p in inp.s0], -1)
+    s, _ = deer.newton(cell, u, a, s0, tol=0.0, max_iters=cap)
+    ref = [s[..., c].reshape(1, D, T) for c in range(s.shape[-1])]
+    scale = max(1.0, max(float(np.abs(r).max()) for r in ref))
+    assert max_err(got, ref) < 1e-4 * scale
