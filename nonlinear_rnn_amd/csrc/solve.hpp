@@ -337,20 +337,30 @@ __device__ __forceinline__ void look_back(const SolveArgs &A, int64_t ch, int32_
 // block stopped by q (a stopped block's carry-out is zero): the same carry
 // look_back() returns at q.  Lane q holds the carry of iteration q, so the
 // Newton loop reads it with readlane instead of one round trip to the
-// predecessors' records per iteration.  Returns false (nothing loaded) when
-// a predecessor is still running, when there are more than kPreloadBlocks
-// predecessors, or when iterations would not fit one lane each.
+// predecessors' records per iteration.  `v` holds the predecessors' flags
+// as preload_flags() loaded them when the block started (lane p: block p).
+// Returns false (nothing loaded) when a predecessor was still running then,
+// when there are more than kPreloadBlocks predecessors, or when iterations
+// would not fit one lane each.
 constexpr int32_t kPreloadBlocks = 8;
+
+// The flags preload_carries() decides on, loaded as the block starts and
+// first read at its first carry, so that the load overlaps the first Newton
+// evaluation instead of delaying it; 0 everywhere when no preload is
+// possible.
+__device__ __forceinline__ int32_t preload_flags(const SolveArgs &A, int64_t ch, int32_t k)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (k > kPreloadBlocks || A.cap >= kWave) return 0;
+    return lane < k ? load_flag(A.flags + ch * A.nb + lane) : kStopBase;
+}
 
 template <class M, class V>
 __device__ __forceinline__ bool preload_carries(const SolveArgs &A, int64_t ch, int32_t k,
-                                                V &carry, int32_t &j_last)
+                                                int32_t v, V &carry, int32_t &j_last)
 {
     constexpr int RF = MapRec<M>::kFloats;
     const int lane = threadIdx.x & (kWave - 1);
-    if (k > kPreloadBlocks || A.cap >= kWave) return false;
-    const int32_t *flags = A.flags + ch * A.nb;
-    const int32_t v = lane < k ? load_flag(flags + lane) : kStopBase;
     if (!__all(v >= kStopBase)) return false;
     after_flag();
     const int64_t rstride = (int64_t)(A.cap + 1) * RF;
@@ -407,13 +417,49 @@ struct LoopSmem {
     typename Cell::Map mlds[MAPS_LDS ? K - 1 : 1][MAPS_LDS ? W * kWave : 1];
 };
 
-// Lane's K steps of every gate, pre-scaled for the exp2-based gates.
-template <class Cell, int K, bool BF16>
+// Lane's K steps of every gate, pre-scaled for the exp2-based gates.  In a
+// block wholly inside [0, T) (FULL) on 16-byte vectors, every plane's loads
+// are issued before any is used and without branches, so they are in flight
+// together; guarded per vector, each plane's loads sat in blocks of their own
+// and the compiler waited for one before issuing the next, a memory round
+// trip per vector at every work unit's start.
+template <class Cell, int K, bool BF16, bool FULL>
 __device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uoff, int64_t t0,
                                                  float (&u)[K][Cell::G])
 {
+    constexpr int G = Cell::G;
+    constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte vector
+    if constexpr (FULL && K % E == 0) {
+        if (A.u_vec) {
+            uint4 raw[G][K / E];
 #pragma unroll
-    for (int g = 0; g < Cell::G; ++g) {
+            for (int g = 0; g < G; ++g) {
+                const uint8_t *p = static_cast<const uint8_t *>(A.u[g]) + (uoff + t0) * (BF16 ? 2 : 4);
+#pragma unroll
+                for (int q = 0; q < K / E; ++q) raw[g][q] = reinterpret_cast<const uint4 *>(p)[q];
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float sc = Cell::uscale(g);
+#pragma unroll
+                for (int q = 0; q < K / E; ++q) {
+                    const uint32_t w[4] = {raw[g][q].x, raw[g][q].y, raw[g][q].z, raw[g][q].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (BF16) {
+                            u[8 * q + 2 * j][g] = __uint_as_float(w[j] << 16) * sc;
+                            u[8 * q + 2 * j + 1][g] = __uint_as_float(w[j] & 0xffff0000u) * sc;
+                        } else {
+                            u[4 * q + j][g] = __uint_as_float(w[j]) * sc;
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
         float tmp[K];
         load_steps<K, BF16>(A.u[g], uoff, t0, A.T, A.ust, A.u_vec != 0, tmp);
         const float sc = Cell::uscale(g);
@@ -467,12 +513,15 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     int32_t lb_known = 0;      // this lane's predecessor's stop flag, once seen
     V din_probe = vzero<V>();
     bool stopped_probe = true;
-    // every predecessor already done: all iterations' carries in one load
+    // every predecessor already done when the block started: all
+    // iterations' carries in one load, at the first carry
     V pre_carry = vzero<V>();
     int32_t pre_jlast = 0;
-    const bool pre = multi && k > 0 && preload_carries<M, V>(A, ch, k, pre_carry, pre_jlast);
+    const int32_t pre_flags = (multi && k > 0) ? preload_flags(A, ch, k) : 0;
+    int pre = (multi && k > 0) ? -1 : 0;  // -1: not decided yet
     const auto carry_at = [&](int32_t i, V &din, bool &stopped) {
-        if (pre && i < kWave) {
+        if (pre < 0) pre = preload_carries<M, V>(A, ch, k, pre_flags, pre_carry, pre_jlast) ? 1 : 0;
+        if (pre > 0 && i < kWave) {
             din = readlane_vec(pre_carry, i);
             stopped = pre_jlast <= i;
         } else {
@@ -663,7 +712,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
 
     const typename Cell::Coef cf = Cell::coef(A.a, A.D, d);
     float u[K][G];
-    load_projections<Cell, K, BF16>(A, b * A.usb + d * A.usd, t0, u);
+    load_projections<Cell, K, BF16, FULL>(A, b * A.usb + d * A.usd, t0, u);
 
     // Newton start and the lane's copy of the state just before it.
     const int64_t soff = b * A.ssb + d * A.ssd;

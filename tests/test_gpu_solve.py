@@ -238,6 +238,34 @@ def test_many_channels(cell, dtype, T, KW):
     assert max_err([g[bs, ds] for g in got], ref) < TOL32
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,W", [(2048, 2), (4096, 4)])
+def test_vector_and_scalar_loads_agree(dtype, T, W):
+    """ParaLSTM with one block per channel (T = 64 * 16 * W) and 2200
+    channels: every channel matches the oracle, and the states are bitwise
+    those of the same planes offset by one element, which the kernel reads
+    step by step instead of in 16-byte vectors."""
+    from nonlinear_rnn_amd import pararnn as pr
+    from tests.gpu_util import dev_inputs
+    B, D = 2, 1100
+    assert pr.plan("lstm", pr.make_shape(B, T, D)) == (16, W, 1)
+    inp = make_inputs("lstm", B, T, D, 5100 + T + len(dtype), u_dtype=dtype, s0_std=0.2,
+                      f_bias=1.0)
+    got, info = gpu_solve(inp, 1e-6, 30)
+    assert info["converged"] and info["units"] == B * D
+    assert max_err(got, oracle_states(inp, rounded=True)) < TOL32
+
+    u, a, s0 = dev_inputs(inp)
+    shifted = []
+    for p in u:
+        big = torch.zeros((B, D, T + 1), dtype=p.dtype, device=p.device)
+        big[:, :, 1:] = p
+        shifted.append(big[:, :, 1:])
+    (c, h), info2 = pr.solve_lstm(shifted, a, s0[0], s0[1], tol=1e-6, max_iters=30)
+    assert pr.read_info(info2)["iters_sum"] == info["iters_sum"]
+    assert np.array_equal(c.cpu().numpy(), got[0]) and np.array_equal(h.cpu().numpy(), got[1])
+
+
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 def test_long_sequence_default_tiling(cell):
     """Past 4096 steps: the default time blocks of 4096 steps, a ragged last
