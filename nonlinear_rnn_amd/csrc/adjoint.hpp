@@ -205,7 +205,89 @@ __global__ void __launch_bounds__(W * kWave) adjoint_kernel(AdjArgs A)
     const int64_t soff = b * A.ssb + d * A.ssd;
 
     F fx[K];
-    {
+    // A block wholly inside [0, T) on 16-byte vectors issues every load of
+    // its inputs before using any (no per-vector bounds tests, which would
+    // put each load in a block of its own and make the compiler wait for one
+    // before issuing the next); the general path below serves the rest.
+    constexpr int EU = BF16 ? 8 : 4;
+    bool done = false;
+    if constexpr (K % EU == 0 && K % 4 == 0) {
+        if (A.u_vec && A.s_vec && tb0 + P <= T) {
+            uint4 ru[G][K / EU];
+            float4 rs[S][K / 4], rg[S][K / 4];
+            float first[S];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const uint8_t *p =
+                    static_cast<const uint8_t *>(A.u[g]) + (uoff + t0) * (BF16 ? 2 : 4);
+#pragma unroll
+                for (int q = 0; q < K / EU; ++q) ru[g][q] = reinterpret_cast<const uint4 *>(p)[q];
+            }
+#pragma unroll
+            for (int c = 0; c < S; ++c) {
+                const float *p = A.s[c] + soff + t0;
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q) rs[c][q] = reinterpret_cast<const float4 *>(p)[q];
+                first[c] = *(t0 == 0 ? A.s0[c] + b * A.D + d : A.s[c] + soff + t0 - 1);
+            }
+#pragma unroll
+            for (int c = 0; c < S; ++c) {
+                if (A.gs[c]) {
+                    const float *p = A.gs[c] + soff + t0;
+#pragma unroll
+                    for (int q = 0; q < K / 4; ++q) rg[c][q] = reinterpret_cast<const float4 *>(p)[q];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < K / 4; ++q) rg[c][q] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+            float u[K][G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float sc = Cell::uscale(g);
+#pragma unroll
+                for (int q = 0; q < K / EU; ++q) {
+                    const uint32_t w[4] = {ru[g][q].x, ru[g][q].y, ru[g][q].z, ru[g][q].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (BF16) {
+                            u[8 * q + 2 * j][g] = __uint_as_float(w[j] << 16) * sc;
+                            u[8 * q + 2 * j + 1][g] = __uint_as_float(w[j] & 0xffff0000u) * sc;
+                        } else {
+                            u[4 * q + j][g] = __uint_as_float(w[j]) * sc;
+                        }
+                    }
+                }
+            }
+            V sp[K], gv[K];
+#pragma unroll
+            for (int c = 0; c < S; ++c) {
+                float st[K], gt[K];
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q) {
+                    st[4 * q] = rs[c][q].x;
+                    st[4 * q + 1] = rs[c][q].y;
+                    st[4 * q + 2] = rs[c][q].z;
+                    st[4 * q + 3] = rs[c][q].w;
+                    gt[4 * q] = rg[c][q].x;
+                    gt[4 * q + 1] = rg[c][q].y;
+                    gt[4 * q + 2] = rg[c][q].z;
+                    gt[4 * q + 3] = rg[c][q].w;
+                }
+                // the gradient a continuation of the sequence sends back to s_T
+                if (A.gend[c] && t0 + K == T) gt[K - 1] += A.gend[c][b * A.D + d];
+                vset(sp[0], c, first[c]);
+#pragma unroll
+                for (int kk = 1; kk < K; ++kk) vset(sp[kk], c, st[kk - 1]);
+#pragma unroll
+                for (int kk = 0; kk < K; ++kk) vset(gv[kk], c, gt[kk]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) fx[kk] = Adj::prep(cf, u[kk], sp[kk], gv[kk]);
+            done = true;
+        }
+    }
+    if (!done) {
         float u[K][G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
