@@ -65,6 +65,7 @@ struct SolveArgs {
     int32_t nb;
     int32_t init_from_output;
     int32_t u_vec, s_vec;
+    int32_t defer_flags;  // time blocks: certify each record one pass after storing it
     uint32_t *ticket;
     int32_t *flags;
     float *records;
@@ -617,19 +618,22 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         }
         const uint32_t cbit = bmx < tolb ? 1u : 0u;
         const bool at_cap = (it == A.cap);
-        // The flag that certifies a record is published one full pass later:
-        // flag `it` (records 0..it-1 complete) goes out just before record
-        // `it` is stored, when the stores of record it-1, issued a pass ago,
-        // have long completed, so the wait in publish_flag costs nothing
-        // (waiting for the record just stored stalled this wave for a store
-        // round trip every pass).  A successor still looking back per
-        // iteration sees each record one pass later; one that preloads its
-        // carries only reads the final stop flag.  Every path out of the
-        // loop publishes a flag covering every stored record.
+        // With A.defer_flags the flag that certifies a record is published
+        // one full pass later: flag `it` (records 0..it-1 complete) goes out
+        // just before record `it` is stored, when the stores of record it-1,
+        // issued a pass ago, have long completed, so the wait in publish_flag
+        // costs nothing (waiting for the record just stored stalls this wave
+        // for a store round trip every pass).  That suits successors that
+        // start after their predecessors have finished and preload their
+        // carries (they only read the final stop flag); a successor looking
+        // back every iteration would run a pass behind, so when blocks of
+        // one channel run side by side each record is certified at once.
+        // Every path out of the loop publishes a flag covering every stored
+        // record.
         if (multi && threadIdx.x == 0) {
-            if (it > 0) publish_flag(A.flags + unit, it);
+            if (A.defer_flags && it > 0) publish_flag(A.flags + unit, it);
             rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
-            if (at_cap) publish_flag(A.flags + unit, it + 1);
+            if (!A.defer_flags || at_cap) publish_flag(A.flags + unit, it + 1);
         }
         if (at_cap) break;
         V din = carry_known ? din_probe : vzero<V>();

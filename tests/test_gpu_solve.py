@@ -283,14 +283,17 @@ def test_long_sequence_default_tiling(cell):
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("cap", [2, 3, 4])
-def test_time_blocks_stop_at_cap_after_a_guessed_last_pass(cell, cap):
+@pytest.mark.parametrize("D", [4, 1024])
+def test_time_blocks_stop_at_cap_after_a_guessed_last_pass(cell, cap, D):
     """Time blocks that reach the iteration cap on a residual-only pass (the
     guessed last evaluation: tol < max|r| < sqrt(tol)) still certify every
     record they stored, so successors reading carries iteration by iteration
     finish; the iterate is the oracle's DEER iterate after `cap` updates
-    (blocks that stop earlier differ from it by less than tol)."""
+    (blocks that stop earlier differ from it by less than tol).  With 4
+    channels each record is certified as it is stored; with 1024 (a full
+    ticket group) a pass later."""
     from nonlinear_rnn_amd import pararnn as pr
-    T, D = 3000, 4
+    T = 3000
     inp = make_inputs(cell, 1, T, D, 900 + cap, s0_std=0.3, f_bias=1.0)
     K, W, nb = pr.plan(cell, pr.make_shape(1, T, D), pr.make_newton(1e-6, cap, 4, 1))
     assert nb == 12
