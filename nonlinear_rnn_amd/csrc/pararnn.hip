@@ -114,6 +114,15 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
         }
         if (K == 0) K = tab[pick][0];
         if (W == 0) W = tab[pick][1];
+        // Few ParaGRU channels on a very long sequence: a channel's blocks run
+        // side by side and look back every iteration over all their
+        // predecessors, so fewer, longer blocks (8192 steps, K = 16, W = 8)
+        // pay off once there are more than 8 of 4096 steps (B=1 D=64:
+        // T=65536 0.085 -> 0.075 ms, T=262144 0.297 -> 0.188 ms; at
+        // T=16384, and with 1024 channels, 4096-step blocks stay faster).
+        if (kind == 0 && cell == PARARNN_GRU && opt_k_w_unset(opt) && K == 16 && W == 4 &&
+            sh->T > 8 * (int64_t)kWave * 16 * 4 && sh->B * sh->D < kTicketGroup)
+            W = 8;
         // Past 4096 steps a channel takes time blocks of 4096 steps (K = 16,
         // W = 4): a block whose predecessors are done loads all their carries
         // at once, so more, smaller blocks cost little and hide each other's

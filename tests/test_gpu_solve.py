@@ -281,6 +281,19 @@ def test_long_sequence_default_tiling(cell):
         assert max_err(got, oracle_states(inp, rounded=True)) < TOL32
 
 
+def test_few_channels_long_sequence_default_tiling():
+    """Few ParaGRU channels past 8 blocks of 4096 steps take 8192-step
+    blocks (K = 16, W = 8), the last one ragged; float32 and bf16."""
+    from nonlinear_rnn_amd import pararnn as pr
+    T = 40000
+    assert pr.plan("gru", pr.make_shape(1, T, 8)) == (16, 8, 5)
+    for dt in ("f32", "bf16"):
+        inp = make_inputs("gru", 1, T, 8, 4000 + len(dt), u_dtype=dt, s0_std=0.2)
+        got, info = gpu_solve(inp, 1e-6, 30)
+        assert info["converged"] and info["units"] == 8 * 5
+        assert max_err(got, oracle_states(inp, rounded=True)) < TOL32
+
+
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("cap", [2, 3, 4])
 @pytest.mark.parametrize("D", [4, 1024])
