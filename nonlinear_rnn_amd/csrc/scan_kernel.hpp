@@ -40,13 +40,25 @@ template <>
 struct ScanIo<Map1> {
     using V = Vec1;
     static constexpr int S = 1;
+    // `inside`: the workgroup's block lies inside [0, T) and the planes are
+    // in 16-byte vectors
     template <int K>
     static __device__ __forceinline__ void load(const ScanArgs &A, int64_t off, int64_t t0,
-                                                Map1 (&m)[K])
+                                                bool inside, Map1 (&m)[K])
     {
         float a[K], b[K];
-        load_steps<K, false>(A.A[0], off, t0, A.T, A.ist, A.in_vec != 0, a);
-        load_steps<K, false>(A.b[0], off, t0, A.T, A.ist, A.in_vec != 0, b);
+        bool done = false;
+        if constexpr (K % 4 == 0) {
+            if (inside) {
+                load_steps_inside<K>(A.A[0] + off + t0, a);
+                load_steps_inside<K>(A.b[0] + off + t0, b);
+                done = true;
+            }
+        }
+        if (!done) {
+            load_steps<K, false>(A.A[0], off, t0, A.T, A.ist, A.in_vec != 0, a);
+            load_steps<K, false>(A.b[0], off, t0, A.T, A.ist, A.in_vec != 0, b);
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k) m[k] = {a[k], b[k]};
     }
@@ -57,16 +69,31 @@ struct ScanIo<Map2> {
     static constexpr int S = 2;
     template <int K>
     static __device__ __forceinline__ void load(const ScanArgs &A, int64_t off, int64_t t0,
-                                                Map2 (&m)[K])
+                                                bool inside, Map2 (&m)[K])
     {
         float a00[K], a01[K], a10[K], a11[K], b0[K], b1[K];
-        const bool v = A.in_vec != 0;
-        load_steps<K, false>(A.A[0], off, t0, A.T, A.ist, v, a00);
-        load_steps<K, false>(A.A[1], off, t0, A.T, A.ist, v, a01);
-        load_steps<K, false>(A.A[2], off, t0, A.T, A.ist, v, a10);
-        load_steps<K, false>(A.A[3], off, t0, A.T, A.ist, v, a11);
-        load_steps<K, false>(A.b[0], off, t0, A.T, A.ist, v, b0);
-        load_steps<K, false>(A.b[1], off, t0, A.T, A.ist, v, b1);
+        bool done = false;
+        if constexpr (K % 4 == 0) {
+            if (inside) {
+                const int64_t o = off + t0;
+                load_steps_inside<K>(A.A[0] + o, a00);
+                load_steps_inside<K>(A.A[1] + o, a01);
+                load_steps_inside<K>(A.A[2] + o, a10);
+                load_steps_inside<K>(A.A[3] + o, a11);
+                load_steps_inside<K>(A.b[0] + o, b0);
+                load_steps_inside<K>(A.b[1] + o, b1);
+                done = true;
+            }
+        }
+        if (!done) {
+            const bool v = A.in_vec != 0;
+            load_steps<K, false>(A.A[0], off, t0, A.T, A.ist, v, a00);
+            load_steps<K, false>(A.A[1], off, t0, A.T, A.ist, v, a01);
+            load_steps<K, false>(A.A[2], off, t0, A.T, A.ist, v, a10);
+            load_steps<K, false>(A.A[3], off, t0, A.T, A.ist, v, a11);
+            load_steps<K, false>(A.b[0], off, t0, A.T, A.ist, v, b0);
+            load_steps<K, false>(A.b[1], off, t0, A.T, A.ist, v, b1);
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k) m[k] = {a00[k], a01[k], a10[k], a11[k], b0[k], b1[k]};
     }
@@ -106,7 +133,8 @@ __global__ void __launch_bounds__(W * kWave) scan_kernel(ScanArgs A)
 
     // maps in time order, identity past T; composed in scan order
     M m[K];
-    ScanIo<M>::template load<K>(A, ioff, t0, m);
+    const bool inside = A.in_vec && (int64_t)(k + 1) * P <= T;
+    ScanIo<M>::template load<K>(A, ioff, t0, inside, m);
 #pragma unroll
     for (int kk = 0; kk < K; ++kk) m[kk] = keep_or_identity(m[kk], t0 + kk < T);
     M agg = identity_map(M{});

@@ -166,6 +166,25 @@ __device__ __forceinline__ void load_steps(const void *base, int64_t off, int64_
     }
 }
 
+// K consecutive float32 steps of a plane known to lie inside [0, T) in
+// 16-byte vectors (p at the first step): plain loads with no bounds test, so
+// that several planes' loads are in flight together (a bounds test per
+// vector puts each load in a block of its own, and the compiler waits for
+// one before issuing the next).
+template <int K>
+__device__ __forceinline__ void load_steps_inside(const float *p, float (&out)[K])
+{
+    static_assert(K % 4 == 0, "16-byte vectors");
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+        const float4 v = reinterpret_cast<const float4 *>(p)[q];
+        out[4 * q] = v.x;
+        out[4 * q + 1] = v.y;
+        out[4 * q + 2] = v.z;
+        out[4 * q + 3] = v.w;
+    }
+}
+
 template <int K>
 __device__ __forceinline__ void store_steps(float *p, int64_t t0, int64_t T, int64_t st, bool vec,
                                             const float (&v)[K])
