@@ -34,16 +34,18 @@ def compile_flags():
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-SOURCES = ["pararnn.hip", "inst_gru_f32.hip", "inst_gru_bf16.hip", "inst_lstm_f32.hip",
-           "inst_lstm_bf16.hip", "inst_scan.hip", "inst_seq.hip",
+SOURCES = ["pararnn.hip", "inst_gru_f32.hip", "inst_gru_bf16.hip", "inst_gru_bf16_defer.hip",
+           "inst_lstm_f32.hip", "inst_lstm_bf16.hip", "inst_scan.hip", "inst_seq.hip",
            "inst_project.hip"]
 
-# Per-unit scheduler choice, by measurement: the ParaGRU kernels on bf16
-# projections (the long-sequence, time-blocked solves) run 3% faster when the
-# machine scheduler favours instruction-level parallelism over occupancy
-# (B=4 T=16384 D=4096: 1.354 -> 1.312 ms); the float32 ParaGRU and the
-# ParaLSTM kernels run slower with it (up to 17%) and keep the default.
-EXTRA_FLAGS = {"inst_gru_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-unit scheduler choice, by measurement: the ParaGRU time-block kernel on
+# bf16 projections that the long, many-channel solves use runs 3% faster
+# when the machine scheduler favours instruction-level parallelism over
+# occupancy (B=4 T=16384 D=4096: 1.354 -> 1.312 ms); every other kernel keeps
+# the default (with the ILP scheduler the float32 ParaGRU and the ParaLSTM
+# kernels ran up to 17% slower, and other bf16 ParaGRU tilings spilled up to
+# 24 registers).
+EXTRA_FLAGS = {"inst_gru_bf16_defer.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _run(cmd, verbose):

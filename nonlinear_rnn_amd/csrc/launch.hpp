@@ -30,6 +30,8 @@ inline bool adjoint_tiling_built(bool, int K, int W)
 #define PARARNN_DECLARE_LAUNCHERS(NAME)                                                          \
     hipError_t launch_newton_##NAME(int K, int W, int variant, int64_t groups, hipStream_t st,  \
                                     const SolveArgs &a);                                        \
+    hipError_t launch_newton_defer_##NAME(int K, int W, int variant, int64_t groups,            \
+                                          hipStream_t st, const SolveArgs &a);                  \
     hipError_t launch_adjoint_##NAME(int K, int W, int64_t groups, hipStream_t st,              \
                                      const AdjArgs &a);
 PARARNN_DECLARE_LAUNCHERS(gru_f32)
@@ -53,8 +55,18 @@ hipError_t launch_scan(int S, int K, int W, bool reverse, int64_t groups, hipStr
         X(4, 8) X(8, 1) X(8, 2) X(8, 4) X(8, 8) X(16, 1) X(16, 2) X(16, 4) X(16, 8)
 
 // Newton kernel variants: 0 = any block (ragged T), 1 = blocks wholly inside
-// [0, T), 2 = as 1 with one block per channel (no cross-block code).
-enum { kNewtonAny = 0, kNewtonFull = 1, kNewtonFullSingle = 2 };
+// [0, T), 2 = as 1 with one block per channel (no cross-block code); 3 and 4
+// = 0 and 1 with each time-block record certified a pass after it is stored
+// (built for K = 16, W = 4 only: the long-sequence default with many
+// channels, whose successors start after their predecessors end).
+enum {
+    kNewtonAny = 0,
+    kNewtonFull = 1,
+    kNewtonFullSingle = 2,
+    kNewtonAnyDefer = 3,
+    kNewtonFullDefer = 4
+};
+inline bool newton_defer_built(int K, int W) { return K == 16 && W == 4; }
 
 #define PARARNN_NEWTON_CASE(CELL, BF16, KK, WW)                                                 \
     case KK * 100 + WW:                                                                         \
@@ -80,6 +92,8 @@ enum { kNewtonAny = 0, kNewtonFull = 1, kNewtonFullSingle = 2 };
                                     const SolveArgs &a)                                         \
     {                                                                                           \
         const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
+        if (variant == kNewtonAnyDefer || variant == kNewtonFullDefer)                           \
+            return launch_newton_defer_##NAME(K, W, variant, groups, st, a);                     \
         switch (K * 100 + W) {                                                                  \
             PARARNN_BASE_KW(PARARNN_NEWTON_CASE_##NAME)                                         \
             EXTRA(PARARNN_NEWTON_CASE_##NAME)                                                   \
@@ -97,6 +111,25 @@ enum { kNewtonAny = 0, kNewtonFull = 1, kNewtonFullSingle = 2 };
         default:                                                                                \
             return hipErrorInvalidValue;                                                        \
         }                                                                                       \
+        return hipGetLastError();                                                               \
+    }
+
+// The deferred-certification variants (K = 16, W = 4), in a translation unit
+// of their own where a cell needs other compiler options for them.
+#define PARARNN_DEFINE_DEFER_LAUNCHER(NAME, CELL, BF16)                                          \
+    hipError_t launch_newton_defer_##NAME(int K, int W, int variant, int64_t groups,            \
+                                          hipStream_t st, const SolveArgs &a)                   \
+    {                                                                                           \
+        if (!newton_defer_built(K, W)) return hipErrorInvalidValue;                              \
+        const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
+        if (variant == kNewtonFullDefer)                                                        \
+            hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, true, false, true>), grid,      \
+                               block, 0, st, a);                                                \
+        else if (variant == kNewtonAnyDefer)                                                    \
+            hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, false, false, true>), grid,     \
+                               block, 0, st, a);                                                \
+        else                                                                                    \
+            return hipErrorInvalidValue;                                                        \
         return hipGetLastError();                                                               \
     }
 

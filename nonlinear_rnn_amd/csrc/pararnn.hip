@@ -262,13 +262,6 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
     for (int c = 0; c < S && work; ++c) sv = sv && aligned16(s[c]);
     A.u_vec = uv ? 1 : 0;
     A.s_vec = sv ? 1 : 0;
-    // Tickets hand out time blocks a ticket group (up to kTicketGroup
-    // channels) apart per rank.  A full group spans more workgroups than the
-    // device holds at once, so a block's successor starts about when the
-    // block ends and preloads its carries: certify records a pass late.
-    // With fewer channels a channel's blocks run side by side and look back
-    // every iteration: certify each record at once.
-    A.defer_flags = ((pl.channels + 7) / 8 * 8 >= kTicketGroup) ? 1 : 0;
     char *base = static_cast<char *>(ws);
     if (work && wl.multi > 0) {
         A.ticket = reinterpret_cast<uint32_t *>(base + wl.ticket);
@@ -294,9 +287,17 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
     }
     const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
-    const int variant = sh->T % pl.P != 0 ? kNewtonAny
+    // Tickets hand out time blocks a ticket group (up to kTicketGroup
+    // channels) apart per rank.  A full group spans more workgroups than the
+    // device holds at once, so a block's successor starts about when the
+    // block ends and preloads its carries: certify records a pass late.
+    // With fewer channels a channel's blocks run side by side and look back
+    // every iteration: certify each record at once.
+    const bool defer = pl.nb > 1 && (pl.channels + 7) / 8 * 8 >= kTicketGroup &&
+                       newton_defer_built(pl.K, pl.W);
+    const int variant = sh->T % pl.P != 0 ? (defer ? kNewtonAnyDefer : kNewtonAny)
                         : pl.nb == 1      ? kNewtonFullSingle
-                                          : kNewtonFull;
+                                          : (defer ? kNewtonFullDefer : kNewtonFull);
     hipError_t e;
     if (cell == PARARNN_GRU)
         e = dt == PARARNN_BF16 ? launch_newton_gru_bf16(pl.K, pl.W, variant, groups, strm, A)

@@ -65,7 +65,6 @@ struct SolveArgs {
     int32_t nb;
     int32_t init_from_output;
     int32_t u_vec, s_vec;
-    int32_t defer_flags;  // time blocks: certify each record one pass after storing it
     uint32_t *ticket;
     int32_t *flags;
     float *records;
@@ -492,7 +491,8 @@ __device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uof
 // from the lane's pre-scaled projections `u`, its copy `hin` of the state
 // before its first step and the Newton start `s`; writes the converged states
 // and folds the unit into the info record.
-template <class Cell, int K, int W, bool FULL, bool MAPS_LDS, bool SINGLE>
+// DEFER: time blocks certify each record one pass after storing it (below).
+template <class Cell, int K, int W, bool FULL, bool MAPS_LDS, bool SINGLE, bool DEFER>
 __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32_t k,
                                            const typename Cell::Coef &cf,
                                            const float (&u)[K][Cell::G],
@@ -637,7 +637,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         }
         const uint32_t cbit = bmx < tolb ? 1u : 0u;
         const bool at_cap = (it == A.cap);
-        // With A.defer_flags the flag that certifies a record is published
+        // With DEFER the flag that certifies a record is published
         // one full pass later: flag `it` (records 0..it-1 complete) goes out
         // just before record `it` is stored, when the stores of record it-1,
         // issued a pass ago, have long completed, so the wait in publish_flag
@@ -650,9 +650,9 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         // Every path out of the loop publishes a flag covering every stored
         // record.
         if (multi && threadIdx.x == 0) {
-            if (A.defer_flags && it > 0) publish_flag(A.flags + unit, it);
+            if (DEFER && it > 0) publish_flag(A.flags + unit, it);
             rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
-            if (!A.defer_flags || at_cap) publish_flag(A.flags + unit, it + 1);
+            if (!DEFER || at_cap) publish_flag(A.flags + unit, it + 1);
         }
         if (at_cap) break;
         V din = carry_known ? din_probe : vzero<V>();
@@ -703,7 +703,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 
 // One work unit per workgroup.  Serves every case: several time blocks per
 // channel (dynamic tickets), ragged T, warm starts.
-template <class Cell, int K, int W, bool BF16, bool FULL, bool SINGLE>
+template <class Cell, int K, int W, bool BF16, bool FULL, bool SINGLE, bool DEFER = false>
 __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWavesPerEu))
     newton_kernel(SolveArgs A)
 {
@@ -768,7 +768,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
             for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
         }
     }
-    solve_unit<Cell, K, W, FULL, kMapsLds, SINGLE>(A, ch, k, cf, u, s, hin, sm);
+    solve_unit<Cell, K, W, FULL, kMapsLds, SINGLE, DEFER>(A, ch, k, cf, u, s, hin, sm);
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit
