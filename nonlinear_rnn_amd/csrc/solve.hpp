@@ -413,27 +413,67 @@ struct Slot {
 };
 
 // Where the lane's running compositions wait between up-sweep and down-sweep:
-// in VGPRs, or (ParaGRU: 2 floats per step) in LDS, which frees 2K VGPRs.
-// The last step's composition is the lane aggregate itself and stays in
-// registers, so K - 1 steps go to LDS: 30 KB per 4-wave workgroup at K = 16,
-// which lets 5 such workgroups (5 waves per SIMD) share a CU's 160 KB.
-template <class Cell, int K, int W, bool FULL>
+// in VGPRs, or the first kLdsMaps of them in LDS.  ParaGRU (2 floats per
+// step) keeps all K - 1 in LDS, which frees 2K VGPRs: 30 KB per 4-wave
+// workgroup at K = 16, so that 5 such workgroups (5 waves per SIMD) share a
+// CU's 160 KB; the last step's composition is the lane aggregate itself and
+// stays in registers.  ParaLSTM (6 floats per step) keeps them in VGPRs,
+// except in time blocks at K = 16, whose cross-block code needs the room:
+// 8 of the 15 go to LDS (48 KB per 4-wave workgroup, two workgroups per CU;
+// 96 KB per 8-wave one), where at 256 VGPRs 24-36 registers spilled.
+template <class Cell, int K, int W, bool FULL, bool SINGLE>
 struct MapStore {
-    static constexpr bool kLds =
-        PARARNN_GRU_MAPS_IN_LDS && sizeof(typename Cell::Map) == 8 && K >= 8;
+    static constexpr bool kGru = sizeof(typename Cell::Map) == 8;
+    static constexpr int kLdsMaps =
+        (kGru && PARARNN_GRU_MAPS_IN_LDS && K >= 8) ? K - 1
+        : (!kGru && !SINGLE && K == 16) ? 8
+                                                  : 0;
     // register budget of the unmasked ParaGRU loop
     // (everything else, ParaLSTM included: at most 256 VGPRs, two waves per
     // SIMD; one more register would halve the occupancy)
     static constexpr int kMinWavesPerEu =
-        !(kLds && FULL && K <= 16) ? 2 : (K == 16 && W <= 4) ? PARARNN_GRU_K16_WAVES : 4;
+        !(kGru && kLdsMaps > 0 && FULL && K <= 16) ? 2
+        : (K == 16 && W <= 4)                      ? PARARNN_GRU_K16_WAVES
+                                                   : 4;
+};
+
+// A running composition in LDS, one plane of floats per map component so
+// that a lane's accesses are 8-byte words at an 8-byte stride (no bank
+// conflicts for either map size).
+template <class M, int NL, int N>
+struct MapPlanes;
+template <int NL, int N>
+struct MapPlanes<Map1, NL, N> {
+    float2 v[NL][N];
+    __device__ __forceinline__ void put(int kk, int i, const Map1 &m) { v[kk][i] = make_float2(m.a, m.b); }
+    __device__ __forceinline__ Map1 get(int kk, int i) const
+    {
+        const float2 x = v[kk][i];
+        return {x.x, x.y};
+    }
+};
+template <int NL, int N>
+struct MapPlanes<Map2, NL, N> {
+    float2 v[NL][3][N];
+    __device__ __forceinline__ void put(int kk, int i, const Map2 &m)
+    {
+        v[kk][0][i] = make_float2(m.a00, m.a01);
+        v[kk][1][i] = make_float2(m.a10, m.a11);
+        v[kk][2][i] = make_float2(m.b0, m.b1);
+    }
+    __device__ __forceinline__ Map2 get(int kk, int i) const
+    {
+        const float2 x = v[kk][0][i], y = v[kk][1][i], z = v[kk][2][i];
+        return {x.x, x.y, y.x, y.y, z.x, z.y};
+    }
 };
 
 // LDS of the Newton loop: wave aggregates (double-buffered by iteration
-// parity) and, optionally, the running compositions of steps 0..K-2.
-template <class Cell, int K, int W, bool MAPS_LDS>
+// parity) and the running compositions of steps 0..NL-1.
+template <class Cell, int K, int W, int NL>
 struct LoopSmem {
     Slot<typename Cell::Map> slots[2][W];
-    typename Cell::Map mlds[MAPS_LDS ? K - 1 : 1][MAPS_LDS ? W * kWave : 1];
+    MapPlanes<typename Cell::Map, (NL > 0 ? NL : 1), (NL > 0 ? W * kWave : 1)> mlds;
 };
 
 // Lane's K steps of every gate, pre-scaled for the exp2-based gates.  In a
@@ -492,12 +532,12 @@ __device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uof
 // before its first step and the Newton start `s`; writes the converged states
 // and folds the unit into the info record.
 // DEFER: time blocks certify each record one pass after storing it (below).
-template <class Cell, int K, int W, bool FULL, bool MAPS_LDS, bool SINGLE, bool DEFER>
+template <class Cell, int K, int W, bool FULL, int NL, bool SINGLE, bool DEFER>
 __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32_t k,
                                            const typename Cell::Coef &cf,
                                            const float (&u)[K][Cell::G],
                                            typename Cell::Vec (&s)[K], typename Cell::Vec hin,
-                                           LoopSmem<Cell, K, W, MAPS_LDS> &sm)
+                                           LoopSmem<Cell, K, W, NL> &sm)
 {
     using M = typename Cell::Map;
     using V = typename Cell::Vec;
@@ -526,7 +566,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     // it already has.  The stopping iteration of every unit is the one the
     // full evaluation would give.
     const uint32_t predb = __float_as_uint(A.guess_tol);
-    M m[MAPS_LDS ? 1 : K];  // running composition of the lane's steps 0..kk
+    M m[K];  // running composition of the lane's steps 0..kk (kk >= NL)
     int32_t it = 0;
     uint32_t bmx = 0;
     bool carry_known = false;  // the probe of this iteration already looked back
@@ -610,11 +650,10 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             mxf = resmax(mxf, mk);
             prev = s[kk];
             agg = kk == 0 ? mk : compose(mk, agg);
-            if constexpr (MAPS_LDS) {
-                if (kk < K - 1) sm.mlds[kk][threadIdx.x] = agg;
-            } else {
+            if (kk < NL)
+                sm.mlds.put(kk, threadIdx.x, agg);
+            else
                 m[kk] = agg;
-            }
         }
         // ---- wave scan, then block exchange through LDS
         const M inc = wave_scan_inclusive(agg);
@@ -677,8 +716,8 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         // chain); the last step takes the carry the next lane also sees.
 #pragma unroll
         for (int kk = 0; kk < K - 1; ++kk) {
-            if constexpr (MAPS_LDS)
-                s[kk] = vadd(s[kk], apply(sm.mlds[kk][threadIdx.x], dl));
+            if (kk < NL)
+                s[kk] = vadd(s[kk], apply(sm.mlds.get(kk, threadIdx.x), dl));
             else
                 s[kk] = vadd(s[kk], apply(m[kk], dl));
         }
@@ -704,15 +743,15 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 // One work unit per workgroup.  Serves every case: several time blocks per
 // channel (dynamic tickets), ragged T, warm starts.
 template <class Cell, int K, int W, bool BF16, bool FULL, bool SINGLE, bool DEFER = false>
-__global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWavesPerEu))
+__global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>::kMinWavesPerEu))
     newton_kernel(SolveArgs A)
 {
     using V = typename Cell::Vec;
     constexpr int G = Cell::G, S = Cell::S;
     constexpr int P = W * kWave * K;
-    constexpr bool kMapsLds = MapStore<Cell, K, W, FULL>::kLds;
+    constexpr int kLdsMaps = MapStore<Cell, K, W, FULL, SINGLE>::kLdsMaps;
 
-    __shared__ LoopSmem<Cell, K, W, kMapsLds> sm;
+    __shared__ LoopSmem<Cell, K, W, kLdsMaps> sm;
     __shared__ int64_t s_ticket;
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -768,7 +807,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL>::kMinWa
             for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
         }
     }
-    solve_unit<Cell, K, W, FULL, kMapsLds, SINGLE, DEFER>(A, ch, k, cf, u, s, hin, sm);
+    solve_unit<Cell, K, W, FULL, kLdsMaps, SINGLE, DEFER>(A, ch, k, cf, u, s, hin, sm);
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit
