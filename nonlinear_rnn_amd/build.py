@@ -34,18 +34,18 @@ def compile_flags():
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-SOURCES = ["pararnn.hip", "inst_gru_f32.hip", "inst_gru_bf16.hip", "inst_gru_bf16_defer.hip",
+SOURCES = ["pararnn.hip", "inst_gru_f32.hip", "inst_gru_bf16.hip", "inst_gru_bf16_seq.hip",
            "inst_lstm_f32.hip", "inst_lstm_bf16.hip", "inst_scan.hip", "inst_seq.hip",
            "inst_project.hip"]
 
-# Per-unit scheduler choice, by measurement: the ParaGRU time-block kernel on
-# bf16 projections that the long, many-channel solves use runs 3% faster
-# when the machine scheduler favours instruction-level parallelism over
-# occupancy (B=4 T=16384 D=4096: 1.354 -> 1.312 ms); every other kernel keeps
-# the default (with the ILP scheduler the float32 ParaGRU and the ParaLSTM
-# kernels ran up to 17% slower, and other bf16 ParaGRU tilings spilled up to
-# 24 registers).
-EXTRA_FLAGS = {"inst_gru_bf16_defer.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-unit scheduler choice, by measurement: the block-sequential ParaGRU
+# kernel on bf16 projections that the long, many-channel solves use runs 2%
+# faster when the machine scheduler favours instruction-level parallelism
+# over occupancy (B=4 T=16384 D=4096: 1.208 -> 1.182 ms per step); every
+# other kernel keeps the default (with the ILP scheduler the float32 ParaGRU
+# and the ParaLSTM kernels ran up to 17% slower, and other bf16 ParaGRU
+# tilings spilled up to 24 registers).
+EXTRA_FLAGS = {"inst_gru_bf16_seq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _run(cmd, verbose):

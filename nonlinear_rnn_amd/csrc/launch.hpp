@@ -30,8 +30,8 @@ inline bool adjoint_tiling_built(bool, int K, int W)
 #define PARARNN_DECLARE_LAUNCHERS(NAME)                                                          \
     hipError_t launch_newton_##NAME(int K, int W, int variant, int64_t groups, hipStream_t st,  \
                                     const SolveArgs &a);                                        \
-    hipError_t launch_newton_defer_##NAME(int K, int W, int variant, int64_t groups,            \
-                                          hipStream_t st, const SolveArgs &a);                  \
+    hipError_t launch_newton_seq_##NAME(int K, int W, int variant, int64_t groups,              \
+                                        hipStream_t st, const SolveArgs &a);                    \
     hipError_t launch_adjoint_##NAME(int K, int W, int64_t groups, hipStream_t st,              \
                                      const AdjArgs &a);
 PARARNN_DECLARE_LAUNCHERS(gru_f32)
@@ -56,17 +56,17 @@ hipError_t launch_scan(int S, int K, int W, bool reverse, int64_t groups, hipStr
 
 // Newton kernel variants: 0 = any block (ragged T), 1 = blocks wholly inside
 // [0, T), 2 = as 1 with one block per channel (no cross-block code); 3 and 4
-// = 0 and 1 with each time-block record certified a pass after it is stored
-// (built for K = 16, W = 4 only: the long-sequence default with many
-// channels, whose successors start after their predecessors end).
+// = 0 and 1 with block-sequential time blocks (built for K = 16, W = 4 only:
+// the long-sequence default with many channels, whose blocks are handed out
+// about when their predecessors end).
 enum {
     kNewtonAny = 0,
     kNewtonFull = 1,
     kNewtonFullSingle = 2,
-    kNewtonAnyDefer = 3,
-    kNewtonFullDefer = 4
+    kNewtonAnySeq = 3,
+    kNewtonFullSeq = 4
 };
-inline bool newton_defer_built(int K, int W) { return K == 16 && W == 4; }
+inline bool newton_seq_built(int K, int W) { return K == 16 && W == 4; }
 
 #define PARARNN_NEWTON_CASE(CELL, BF16, KK, WW)                                                 \
     case KK * 100 + WW:                                                                         \
@@ -92,8 +92,8 @@ inline bool newton_defer_built(int K, int W) { return K == 16 && W == 4; }
                                     const SolveArgs &a)                                         \
     {                                                                                           \
         const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
-        if (variant == kNewtonAnyDefer || variant == kNewtonFullDefer)                           \
-            return launch_newton_defer_##NAME(K, W, variant, groups, st, a);                     \
+        if (variant == kNewtonAnySeq || variant == kNewtonFullSeq)                               \
+            return launch_newton_seq_##NAME(K, W, variant, groups, st, a);                       \
         switch (K * 100 + W) {                                                                  \
             PARARNN_BASE_KW(PARARNN_NEWTON_CASE_##NAME)                                         \
             EXTRA(PARARNN_NEWTON_CASE_##NAME)                                                   \
@@ -114,18 +114,18 @@ inline bool newton_defer_built(int K, int W) { return K == 16 && W == 4; }
         return hipGetLastError();                                                               \
     }
 
-// The deferred-certification variants (K = 16, W = 4), in a translation unit
-// of their own where a cell needs other compiler options for them.
-#define PARARNN_DEFINE_DEFER_LAUNCHER(NAME, CELL, BF16)                                          \
-    hipError_t launch_newton_defer_##NAME(int K, int W, int variant, int64_t groups,            \
-                                          hipStream_t st, const SolveArgs &a)                   \
+// The block-sequential variants (K = 16, W = 4), in a translation unit of
+// their own where a cell needs other compiler options for them.
+#define PARARNN_DEFINE_SEQ_LAUNCHER(NAME, CELL, BF16)                                            \
+    hipError_t launch_newton_seq_##NAME(int K, int W, int variant, int64_t groups,              \
+                                        hipStream_t st, const SolveArgs &a)                     \
     {                                                                                           \
-        if (!newton_defer_built(K, W)) return hipErrorInvalidValue;                              \
+        if (!newton_seq_built(K, W)) return hipErrorInvalidValue;                                \
         const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
-        if (variant == kNewtonFullDefer)                                                        \
+        if (variant == kNewtonFullSeq)                                                          \
             hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, true, false, true>), grid,      \
                                block, 0, st, a);                                                \
-        else if (variant == kNewtonAnyDefer)                                                    \
+        else if (variant == kNewtonAnySeq)                                                      \
             hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, false, false, true>), grid,     \
                                block, 0, st, a);                                                \
         else                                                                                    \

@@ -289,15 +289,16 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
     const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
     // Tickets hand out time blocks a ticket group (up to kTicketGroup
     // channels) apart per rank.  A full group spans more workgroups than the
-    // device holds at once, so a block's successor starts about when the
-    // block ends and preloads its carries: certify records a pass late.
-    // With fewer channels a channel's blocks run side by side and look back
-    // every iteration: certify each record at once.
-    const bool defer = pl.nb > 1 && (pl.channels + 7) / 8 * 8 >= kTicketGroup &&
-                       newton_defer_built(pl.K, pl.W);
-    const int variant = sh->T % pl.P != 0 ? (defer ? kNewtonAnyDefer : kNewtonAny)
+    // device holds at once, so a block is handed out about when its
+    // predecessor ends: solve the blocks one after the other, each from its
+    // predecessor's converged last state (no per-iteration carries).  With
+    // fewer channels a channel's blocks run side by side as one Newton
+    // iteration over the whole sequence.
+    const bool seq = pl.nb > 1 && (pl.channels + 7) / 8 * 8 >= kTicketGroup &&
+                     newton_seq_built(pl.K, pl.W);
+    const int variant = sh->T % pl.P != 0 ? (seq ? kNewtonAnySeq : kNewtonAny)
                         : pl.nb == 1      ? kNewtonFullSingle
-                                          : (defer ? kNewtonFullDefer : kNewtonFull);
+                                          : (seq ? kNewtonFullSeq : kNewtonFull);
     hipError_t e;
     if (cell == PARARNN_GRU)
         e = dt == PARARNN_BF16 ? launch_newton_gru_bf16(pl.K, pl.W, variant, groups, strm, A)

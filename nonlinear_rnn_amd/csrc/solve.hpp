@@ -531,8 +531,8 @@ __device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uof
 // from the lane's pre-scaled projections `u`, its copy `hin` of the state
 // before its first step and the Newton start `s`; writes the converged states
 // and folds the unit into the info record.
-// DEFER: time blocks certify each record one pass after storing it (below).
-template <class Cell, int K, int W, bool FULL, int NL, bool SINGLE, bool DEFER>
+// SEQ: block-sequential time blocks (no carries; see newton_kernel).
+template <class Cell, int K, int W, bool FULL, int NL, bool SINGLE, bool SEQ>
 __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32_t k,
                                            const typename Cell::Coef &cf,
                                            const float (&u)[K][Cell::G],
@@ -551,7 +551,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     const int64_t T = A.T;
     const int64_t tb0 = (int64_t)k * P;
     const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
-    const bool multi = !SINGLE && A.nb > 1;
+    const bool multi = !SINGLE && !SEQ && A.nb > 1;
     const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
     const bool full = FULL || tb0 + P <= T;  // uniform over the workgroup
 
@@ -615,11 +615,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 #pragma unroll
             for (int j = 1; j < W; ++j) bmx = max(bmx, sm.slots[xp][j].mx);
             xp ^= 1;
-            if (it == A.cap) {
-                // records 0..cap-1 are stored (one per full pass)
-                if (multi && threadIdx.x == 0) publish_flag(A.flags + unit, it);
-                break;
-            }
+            if (it == A.cap) break;
             if (bmx < tolb) {
                 if (!multi) break;
                 if (k > 0) carry_at(it, din_probe, stopped_probe);
@@ -676,22 +672,11 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         }
         const uint32_t cbit = bmx < tolb ? 1u : 0u;
         const bool at_cap = (it == A.cap);
-        // With DEFER the flag that certifies a record is published
-        // one full pass later: flag `it` (records 0..it-1 complete) goes out
-        // just before record `it` is stored, when the stores of record it-1,
-        // issued a pass ago, have long completed, so the wait in publish_flag
-        // costs nothing (waiting for the record just stored stalls this wave
-        // for a store round trip every pass).  That suits successors that
-        // start after their predecessors have finished and preload their
-        // carries (they only read the final stop flag); a successor looking
-        // back every iteration would run a pass behind, so when blocks of
-        // one channel run side by side each record is certified at once.
-        // Every path out of the loop publishes a flag covering every stored
-        // record.
+        // Each record is certified by a flag as soon as it is stored (the
+        // flag store waits for the record's stores to complete).
         if (multi && threadIdx.x == 0) {
-            if (DEFER && it > 0) publish_flag(A.flags + unit, it);
             rec_store(A.records + (unit * (int64_t)(A.cap + 1) + it) * RF, blk, cbit);
-            if (!DEFER || at_cap) publish_flag(A.flags + unit, it + 1);
+            publish_flag(A.flags + unit, it + 1);
         }
         if (at_cap) break;
         V din = carry_known ? din_probe : vzero<V>();
@@ -733,6 +718,18 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         for (int kk = 0; kk < K; ++kk) tmp[kk] = vget(s[kk], c);
         store_steps<K>(A.s[c] + soff, t0, T, A.sst, A.s_vec != 0, tmp);
     }
+    // Block-sequential time blocks: hand the block's last state to the
+    // successor through the unit's record (device-coherent stores: the
+    // state planes' plain stores may sit in this XCD's L2, which another
+    // XCD does not see), then the stop flag (its store waits for them).
+    if constexpr (SEQ) {
+        if (last_lane_of_block) {
+            float *rec = A.records + unit * (int64_t)(A.cap + 1) * RF;
+#pragma unroll
+            for (int c = 0; c < S; ++c) store_relaxed(rec + c, vget(s[K - 1], c));
+            publish_flag(A.flags + unit, kStopBase + it);
+        }
+    }
     // The unit's own convergence record, folded into the info record by a
     // separate pass: atomics on one shared record from every workgroup
     // serialise on a single address and stall the whole solve.
@@ -742,7 +739,19 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
 
 // One work unit per workgroup.  Serves every case: several time blocks per
 // channel (dynamic tickets), ragged T, warm starts.
-template <class Cell, int K, int W, bool BF16, bool FULL, bool SINGLE, bool DEFER = false>
+// SEQ (time blocks of many channels): block-sequential.  Block k > 0 waits
+// until block k-1 of its channel has converged and stored its states, then
+// solves its own Newton system from the exact state before it (block k-1's
+// last state, handed over in block k-1's record): no per-iteration carries
+// or look-back.  Every block
+// still stops only when its own max |r_t| < tol, the residual of its first
+// step taken against that state, so the whole trajectory meets the stopping
+// rule; the iterates differ from one Newton iteration over the whole
+// sequence, the converged states agree with it to within the tolerance.
+// Rank-spaced tickets hand a block out about when its predecessor ends, so
+// the wait is short; every predecessor holds a smaller ticket, so it is
+// resident or done and the waits cannot deadlock.
+template <class Cell, int K, int W, bool BF16, bool FULL, bool SINGLE, bool SEQ = false>
 __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>::kMinWavesPerEu))
     newton_kernel(SolveArgs A)
 {
@@ -807,7 +816,20 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>
             for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
         }
     }
-    solve_unit<Cell, K, W, FULL, kLdsMaps, SINGLE, DEFER>(A, ch, k, cf, u, s, hin, sm);
+    if constexpr (SEQ) {
+        if (k > 0 && wave == 0) {
+            const int32_t *pred = A.flags + unit - 1;
+            while (load_flag(pred) < kStopBase) __builtin_amdgcn_s_sleep(2);
+            after_flag();
+            if (lane == 0) {
+                const float *rec =
+                    A.records + (unit - 1) * (int64_t)(A.cap + 1) * MapRec<typename Cell::Map>::kFloats;
+#pragma unroll
+                for (int c = 0; c < S; ++c) vset(hin, c, load_relaxed(rec + c));
+            }
+        }
+    }
+    solve_unit<Cell, K, W, FULL, kLdsMaps, SINGLE, SEQ>(A, ch, k, cf, u, s, hin, sm);
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit

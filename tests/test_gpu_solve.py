@@ -296,17 +296,14 @@ def test_few_channels_long_sequence_default_tiling():
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("cap", [2, 3, 4])
-@pytest.mark.parametrize("D", [4, 1024])
-def test_time_blocks_stop_at_cap_after_a_guessed_last_pass(cell, cap, D):
+def test_time_blocks_stop_at_cap_after_a_guessed_last_pass(cell, cap):
     """Time blocks that reach the iteration cap on a residual-only pass (the
     guessed last evaluation: tol < max|r| < sqrt(tol)) still certify every
     record they stored, so successors reading carries iteration by iteration
     finish; the iterate is the oracle's DEER iterate after `cap` updates
-    (blocks that stop earlier differ from it by less than tol).  With 4
-    channels each record is certified as it is stored; with 1024 (a full
-    ticket group) a pass later."""
+    (blocks that stop earlier differ from it by less than tol)."""
     from nonlinear_rnn_amd import pararnn as pr
-    T = 3000
+    T, D = 3000, 4
     inp = make_inputs(cell, 1, T, D, 900 + cap, s0_std=0.3, f_bias=1.0)
     K, W, nb = pr.plan(cell, pr.make_shape(1, T, D), pr.make_newton(1e-6, cap, 4, 1))
     assert nb == 12
@@ -319,3 +316,48 @@ def test_time_blocks_stop_at_cap_after_a_guessed_last_pass(cell, cap, D):
     ref = [s[..., c].reshape(1, D, T) for c in range(s.shape[-1])]
     scale = max(1.0, max(float(np.abs(r).max()) for r in ref))
     assert max_err(got, ref) < 1e-4 * scale
+
+
+def block_sequential_deer(cell, inp, P, cap):
+    """The oracle's DEER iterates block by block: each time block of P steps
+    is its own Newton solve (tol = 0, `cap` updates from zero), started from
+    the previous block's final state."""
+    B, D, T = inp.u[0].shape
+    u = deer.from_planes(inp.u)
+    a = deer.a_per_channel(inp.a, B)
+    st = np.stack([p.reshape(-1).astype(np.float64) for p in inp.s0], -1)
+    parts = []
+    for t0 in range(0, T, P):
+        s, _ = deer.newton(cell, u[:, t0:t0 + P], a, st, tol=0.0, max_iters=cap)
+        parts.append(s)
+        st = s[:, -1]
+    s = np.concatenate(parts, axis=1)
+    return [s[..., c].reshape(B, D, T) for c in range(s.shape[-1])]
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("T", [8192, 9000])
+def test_block_sequential_time_blocks(cell, T):
+    """1024 channels (a full ticket group) past 4096 steps: blocks of 4096
+    steps solved one after the other, each from its predecessor's converged
+    last state.  Every channel matches the sequential oracle; results are
+    bitwise repeatable; with tol = 0 and a cap the iterates are the
+    block-by-block DEER iterates."""
+    from nonlinear_rnn_amd import pararnn as pr
+    B, D = 1, 1024
+    K, W, nb = pr.plan(cell, pr.make_shape(B, T, D))
+    assert (K, W, nb) == (16, 4, -(-T // 4096))
+    inp = make_inputs(cell, B, T, D, 7100 + T, s0_std=0.2, f_bias=1.0)
+    got, info = gpu_solve(inp, 1e-6, 30)
+    assert info["converged"] and info["units"] == D * nb and info["max_abs_res"] < 1e-6
+    assert max_err(got, oracle_states(inp)) < TOL32
+    again, info2 = gpu_solve(inp, 1e-6, 30)
+    for x, y in zip(got, again):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    assert info2 == info
+    cap = 3
+    capped, info3 = gpu_solve(inp, 0.0, cap)
+    assert info3["iters"] == cap and not info3["converged"]
+    ref = block_sequential_deer(cell, inp, 4096, cap)
+    scale = max(1.0, max(float(np.abs(r).max()) for r in ref))
+    assert max_err(capped, ref) < 1e-4 * scale
