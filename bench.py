@@ -514,8 +514,11 @@ def measure_solve(w, key, args, flush_buf, headline):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    # the roofline region: K steps, the MALL evicted before each one
+    # the roofline region: K steps, the MALL evicted before each one (the
+    # eviction buffer written once beforehand, so that no first touch of
+    # its pages falls inside the region)
     cold = events()
+    flush_mall(flush_buf)
     torch.cuda.synchronize()
     run(cold, True)
     torch.cuda.synchronize()
@@ -525,6 +528,7 @@ def measure_solve(w, key, args, flush_buf, headline):
         ms = [ev[i].elapsed_time(ev[i + 1]) for ev in cold]
         avg = sum(ms) / len(ms)
         return {"kernel": name, "ms_avg": avg, "ms_min": min(ms),
+                "ms_median": sorted(ms)[len(ms) // 2],
                 "ms_avg_back_to_back": sum(warm) / len(warm), "bytes": nbytes,
                 "achieved": nbytes / (avg * 1e-3) / 1e9,
                 "hbm_frac": nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}

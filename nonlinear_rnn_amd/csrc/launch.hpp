@@ -30,8 +30,8 @@ inline bool adjoint_tiling_built(bool, int K, int W)
 #define PARARNN_DECLARE_LAUNCHERS(NAME)                                                          \
     hipError_t launch_newton_##NAME(int K, int W, int variant, int64_t groups, hipStream_t st,  \
                                     const SolveArgs &a);                                        \
-    hipError_t launch_newton_seq_##NAME(int K, int W, int variant, int64_t groups,              \
-                                        hipStream_t st, const SolveArgs &a);                    \
+    hipError_t launch_newton_seq_##NAME(int K, int W, int64_t groups, hipStream_t st,          \
+                                        const SolveArgs &a);                                    \
     hipError_t launch_adjoint_##NAME(int K, int W, int64_t groups, hipStream_t st,              \
                                      const AdjArgs &a);
 PARARNN_DECLARE_LAUNCHERS(gru_f32)
@@ -92,8 +92,13 @@ inline bool newton_seq_built(int K, int W) { return K == 16 && W == 4; }
                                     const SolveArgs &a)                                         \
     {                                                                                           \
         const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
-        if (variant == kNewtonAnySeq || variant == kNewtonFullSeq)                               \
-            return launch_newton_seq_##NAME(K, W, variant, groups, st, a);                       \
+        if (variant == kNewtonFullSeq) return launch_newton_seq_##NAME(K, W, groups, st, a);     \
+        if (variant == kNewtonAnySeq) {                                                         \
+            if (!newton_seq_built(K, W)) return hipErrorInvalidValue;                            \
+            hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, false, false, true>), grid,     \
+                               block, 0, st, a);                                                \
+            return hipGetLastError();                                                           \
+        }                                                                                       \
         switch (K * 100 + W) {                                                                  \
             PARARNN_BASE_KW(PARARNN_NEWTON_CASE_##NAME)                                         \
             EXTRA(PARARNN_NEWTON_CASE_##NAME)                                                   \
@@ -114,22 +119,17 @@ inline bool newton_seq_built(int K, int W) { return K == 16 && W == 4; }
         return hipGetLastError();                                                               \
     }
 
-// The block-sequential variants (K = 16, W = 4), in a translation unit of
-// their own where a cell needs other compiler options for them.
+// The block-sequential kernel on full blocks (K = 16, W = 4), in a
+// translation unit of its own where a cell needs other compiler options for
+// it (the ragged-T variant is launched with the other kernels).
 #define PARARNN_DEFINE_SEQ_LAUNCHER(NAME, CELL, BF16)                                            \
-    hipError_t launch_newton_seq_##NAME(int K, int W, int variant, int64_t groups,              \
-                                        hipStream_t st, const SolveArgs &a)                     \
+    hipError_t launch_newton_seq_##NAME(int K, int W, int64_t groups, hipStream_t st,          \
+                                        const SolveArgs &a)                                     \
     {                                                                                           \
         if (!newton_seq_built(K, W)) return hipErrorInvalidValue;                                \
         const dim3 grid((unsigned)groups), block((unsigned)(kWave * W));                        \
-        if (variant == kNewtonFullSeq)                                                          \
-            hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, true, false, true>), grid,      \
-                               block, 0, st, a);                                                \
-        else if (variant == kNewtonAnySeq)                                                      \
-            hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, false, false, true>), grid,     \
-                               block, 0, st, a);                                                \
-        else                                                                                    \
-            return hipErrorInvalidValue;                                                        \
+        hipLaunchKernelGGL((newton_kernel<CELL, 16, 4, BF16, true, false, true>), grid, block,   \
+                           0, st, a);                                                           \
         return hipGetLastError();                                                               \
     }
 

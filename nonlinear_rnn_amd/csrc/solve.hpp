@@ -597,16 +597,17 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             // after a wrong guess must not look alike to the compiler, or it
             // keeps all K steps' gate values live into the full pass.  One
             // side passes its states through an empty asm: the full pass, in
-            // place (one workgroup per channel: fewer registers and moves),
-            // or this one (time blocks: measured faster there).
+            // place (one workgroup per channel or block-sequential blocks:
+            // fewer registers and moves), or this one (blocks exchanging
+            // carries: measured faster there).
             float mxf = 0.0f;
-            V prev = SINGLE ? hin : opaque(hin);
+            V prev = (SINGLE || SEQ) ? hin : opaque(hin);
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) {
                 V rk = Cell::step_residual(cf, u[kk], prev, s[kk]);
                 if (!full) rk = keep_or_zero(rk, t0 + kk < T);
                 mxf = resmax(mxf, rk);
-                prev = SINGLE ? s[kk] : opaque(s[kk]);
+                prev = (SINGLE || SEQ) ? s[kk] : opaque(s[kk]);
             }
             const uint32_t wmx = wave_max_to_last(__float_as_uint(mxf));
             if (lane == kWave - 1) sm.slots[xp][wave].mx = wmx;
@@ -626,7 +627,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
                 carry_known = true;
             }
             // not yet: full evaluation of the same iterate
-            if constexpr (SINGLE) {
+            if constexpr (SINGLE || SEQ) {
                 hin = opaque(hin);
 #pragma unroll
                 for (int kk = 0; kk < K; ++kk) s[kk] = opaque(s[kk]);
