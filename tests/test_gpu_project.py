@@ -35,7 +35,11 @@ def check(got, x64, w64, bias, out_bf16=False):
 
 @pytest.mark.parametrize("B,T,I,M", [(2, 128, 64, 256), (1, 100, 40, 300), (3, 257, 1024, 288),
                                      (2, 384, 96, 768), (1, 1, 8, 1), (2, 130, 33, 257),
-                                     (2, 700, 192, 600), (1, 2100, 128, 1100)])
+                                     (2, 700, 192, 600), (1, 2100, 128, 1100),
+                                     # more tiles than compute units, ragged in m and t:
+                                     # 408 tiles (a multiple of the 8 XCDs) with one k
+                                     # step, 306 tiles (not a multiple) with two
+                                     (4, 4100, 64, 1300), (3, 4100, 128, 1300)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_project_parity(B, T, I, M, out_dtype):
     rng = np.random.default_rng(B * 1000 + T + I + M)
