@@ -323,7 +323,7 @@ def block_sequential_deer(cell, inp, P, cap):
     is its own Newton solve (tol = 0, `cap` updates from zero), started from
     the previous block's final state."""
     B, D, T = inp.u[0].shape
-    u = deer.from_planes(inp.u)
+    u = deer.from_planes(inp.u_rounded)
     a = deer.a_per_channel(inp.a, B)
     st = np.stack([p.reshape(-1).astype(np.float64) for p in inp.s0], -1)
     parts = []
@@ -337,17 +337,20 @@ def block_sequential_deer(cell, inp, P, cap):
 
 @pytest.mark.parametrize("cell", ["gru", "lstm"])
 @pytest.mark.parametrize("T", [8192, 9000])
-def test_block_sequential_time_blocks(cell, T):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_sequential_time_blocks(cell, T, dtype):
     """1024 channels (a full ticket group) past 4096 steps: blocks of 4096
     steps solved one after the other, each from its predecessor's converged
-    last state.  Every channel matches the sequential oracle; results are
+    last state, on float32 and bf16 projections, full blocks and a ragged
+    last one.  Every channel matches the sequential oracle; results are
     bitwise repeatable; with tol = 0 and a cap the iterates are the
     block-by-block DEER iterates."""
     from nonlinear_rnn_amd import pararnn as pr
     B, D = 1, 1024
     K, W, nb = pr.plan(cell, pr.make_shape(B, T, D))
     assert (K, W, nb) == (16, 4, -(-T // 4096))
-    inp = make_inputs(cell, B, T, D, 7100 + T, s0_std=0.2, f_bias=1.0)
+    inp = make_inputs(cell, B, T, D, 7100 + T + len(dtype), u_dtype=dtype, s0_std=0.2,
+                      f_bias=1.0)
     got, info = gpu_solve(inp, 1e-6, 30)
     assert info["converged"] and info["units"] == D * nb and info["max_abs_res"] < 1e-6
     assert max_err(got, oracle_states(inp)) < TOL32
