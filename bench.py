@@ -271,6 +271,90 @@ def bench_project(w, args):
     }, **extra)
 
 
+def bench_scan(w, args):
+    """The standalone linear-recurrence scan x_t = A_t x_{t-1} + b_t over the
+    workload's channels and length, with the workload's state size (S = 1
+    for ParaGRU, 2 for ParaLSTM): A ~ U(0, 0.9) (S*S planes, contracting), b
+    ~ N(0, 1) (S planes), x0 = 0.  One step = one forward scan; a reverse
+    scan is timed beside it.  HBM roof: A and b read once, x written once."""
+    import torch
+    from nonlinear_rnn_amd import pararnn as pr
+
+    dev = "cuda:0"
+    S = w.S
+    gen = torch.Generator(device="cpu").manual_seed(w.seed + 300)
+    A = [(torch.rand((w.B, w.D, w.T), generator=gen) * 0.9).to(dev) for _ in range(S * S)]
+    b = [torch.randn((w.B, w.D, w.T), generator=gen).to(dev) for _ in range(S)]
+    out = [torch.empty((w.B, w.D, w.T), device=dev) for _ in range(S)]
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+
+    def run(rev):
+        pr.scan(A, b, reverse=rev, out=out, stream=stream)
+
+    settle(lambda: run(False), args)
+    for _ in range(args.warmup):
+        run(False)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        run(False)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    b2b = [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    def evicted(rev):
+        ms = []
+        for _ in range(args.steps):
+            flush_mall(flush_buf)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(rev)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return ms
+
+    fwd, rev = evicted(False), evicted(True)
+    extra = {}
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = n * 4
+    nbytes = (S * S + 2 * S) * 4 * w.N
+    kavg = sum(fwd) / len(fwd)
+    ravg = sum(rev) / len(rev)
+    gbs = nbytes / (kavg * 1e-3) / 1e9
+    ms_per_step = wall * 1e3 / args.steps
+    return {
+        "metric": "linear-recurrence scan elems/sec (B·T·D) + % of MI355X HBM peak",
+        "value": w.N / (ms_per_step * 1e-3), "unit": "elem/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": f"synthetic (torch seed {w.seed + 300}: A~U(0,0.9), b~N(0,1), x0=0)",
+        "config": {"workload": f"scan, state size {S}, over the channels of {w.name}",
+                   "B": w.B, "T": w.T, "D": w.D, "S": S},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("scan_" + args.workload),
+                     "algorithmic_bytes": nbytes, "kernel": "scan_kernel",
+                     "kernel_ms_avg": kavg, "kernel_ms_min": min(fwd),
+                     "kernel_ms_avg_back_to_back": sum(b2b) / len(b2b),
+                     "timing": f"HIP events on the launch stream, {args.steps} launches, a "
+                               f"{args.flush_mib} MiB write before each (outside the event pair)"},
+        "reverse": {"kernel_ms_avg": ravg, "achieved": nbytes / (ravg * 1e-3) / 1e9,
+                    "frac": nbytes / (ravg * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        **extra,
+    }
+
+
 def bench_checkpoint(w, args):
     """Training step (forward solve + backward through torch.autograd) on
     the workload, one-piece vs checkpointed in time chunks of --chunk steps:
@@ -608,9 +692,11 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="size of the buffer written before every step of the roofline "
                          "region (evicts the 256 MB MALL); at least 512")
-    ap.add_argument("--op", choices=["solve", "project", "checkpoint", "speedup"], default="solve",
+    ap.add_argument("--op", choices=["solve", "project", "scan", "checkpoint", "speedup"],
+                    default="solve",
                     help="solve: the Newton solve (default); project: the input projection "
-                         "u = W x + b for the workload's shapes with I = D inputs; "
+                         "u = W x + b for the workload's shapes with I = D inputs; scan: the "
+                         "standalone linear-recurrence scan over the workload's channels; "
                          "checkpoint: a training step one-piece vs checkpointed in time "
                          "chunks (--chunk); speedup: Newton vs sequential application on "
                          "the same GPU, 64 channels, growing T")
@@ -646,6 +732,9 @@ def main():
     w = WORKLOADS[args.workload]
     if args.op == "project":
         print(json.dumps(bench_project(w, args)), flush=True)
+        return
+    if args.op == "scan":
+        print(json.dumps(bench_scan(w, args)), flush=True)
         return
     if args.op == "checkpoint":
         print(json.dumps(bench_checkpoint(w, args)), flush=True)
