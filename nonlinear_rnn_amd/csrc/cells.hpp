@@ -88,6 +88,19 @@ struct GruCell {
         const float J = fmaf_(z, fmaf_(cmh * omz, p.az, dcr), omz);
         return {J, b};
     }
+    // step_map at h_{t-1} = h_t = 0 (every step of the zero Newton start but
+    // a lane's first): the terms with h drop out exactly, so the values are
+    // those of step_map bit for bit — z = sig(u_z), r = sig(u_r),
+    // c = tanh(u_c), b = z c, df/dh = (1 - z) + z [c (1 - z) a_z + (1 - c^2) a_c r].
+    static constexpr bool kZeroPass = true;
+    static __device__ __forceinline__ Map1 step_map_zero(const Coef &p, const float (&u)[G])
+    {
+        const float z = sigmoid_q(u[0]), r = sigmoid_q(u[1]), c = tanh_q(u[2]);
+        const float omz = 1.0f - z;
+        const float dcr = (fmaf_(-c, c, 1.0f) * p.ac) * r;
+        const float J = fmaf_(z, fmaf_(c * omz, p.az, dcr), omz);
+        return {J, fmaf_(z, c, 0.0f)};
+    }
 };
 
 // ----------------------------------------------------------- ParaLSTM ----
@@ -115,6 +128,9 @@ struct LstmCell {
     }
     static __device__ __forceinline__ float uscale(int g) { return g == 2 ? -2.0f * kLog2e : -kLog2e; }
 
+    // No zero-start first pass: with every step's gates depending on u alone
+    // the scheduler hoists them all and the one-block kernels spill.
+    static constexpr bool kZeroPass = false;
     struct Gates {
         float i, f, g, o, c, tc;  // gates, c' and tanh(c')
     };

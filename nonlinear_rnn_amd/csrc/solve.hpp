@@ -640,9 +640,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         float mxf = 0.0f;
         M agg = identity_map(M{});
         V prev = hin;
-#pragma unroll
-        for (int kk = 0; kk < K; ++kk) {
-            M mk = Cell::step_map(cf, u[kk], prev, s[kk]);
+        const auto up = [&](int kk, M mk) {
             if (!full) mk = keep_or_identity(mk, t0 + kk < T);
             mxf = resmax(mxf, mk);
             prev = s[kk];
@@ -651,6 +649,25 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
                 sm.mlds.put(kk, threadIdx.x, agg);
             else
                 m[kk] = agg;
+        };
+        const auto up_all = [&]() {
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) up(kk, Cell::step_map(cf, u[kk], prev, s[kk]));
+        };
+        // (the carry-exchanging kernels would spill with the second loop)
+        if constexpr (Cell::kZeroPass && (SINGLE || SEQ)) {
+            if (it == 0 && !A.init_from_output) {
+                // first evaluation from the zero start: every step but the
+                // lane's first (whose predecessor may be a given state) sees
+                // h_{t-1} = h_t = 0
+                up(0, Cell::step_map(cf, u[0], prev, s[0]));
+#pragma unroll
+                for (int kk = 1; kk < K; ++kk) up(kk, Cell::step_map_zero(cf, u[kk]));
+            } else {
+                up_all();
+            }
+        } else {
+            up_all();
         }
         // ---- wave scan, then block exchange through LDS
         const M inc = wave_scan_inclusive(agg);
