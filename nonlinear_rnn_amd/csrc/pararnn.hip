@@ -280,22 +280,21 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
     };
     if (!work) return fold_info();
 
-    if (pl.nb > 1) {
+    // With a full ticket group of channels (more workgroups than the device
+    // holds at once) every workgroup solves one channel's time blocks one
+    // after the other, each from its predecessor's converged last state (no
+    // per-iteration carries, no tickets or flags).  With fewer channels a
+    // channel's blocks run side by side, in workgroups of their own, as one
+    // Newton iteration over the whole sequence.
+    const bool seq = pl.nb > 1 && (pl.channels + 7) / 8 * 8 >= kTicketGroup &&
+                     newton_seq_built(pl.K, pl.W);
+    if (pl.nb > 1 && !seq) {
         const int tpb = 256;
         hipLaunchKernelGGL(solve_init_kernel, dim3((unsigned)((pl.units + tpb - 1) / tpb)),
                            dim3(tpb), 0, strm, A, S, pl.units, (int32_t)pl.P);
         if (hipGetLastError() != hipSuccess) return PARARNN_ERR_HIP;
     }
-    const int64_t groups = ((pl.channels + 7) / 8) * 8 * pl.nb;
-    // Tickets hand out time blocks a ticket group (up to kTicketGroup
-    // channels) apart per rank.  A full group spans more workgroups than the
-    // device holds at once, so a block is handed out about when its
-    // predecessor ends: solve the blocks one after the other, each from its
-    // predecessor's converged last state (no per-iteration carries).  With
-    // fewer channels a channel's blocks run side by side as one Newton
-    // iteration over the whole sequence.
-    const bool seq = pl.nb > 1 && (pl.channels + 7) / 8 * 8 >= kTicketGroup &&
-                     newton_seq_built(pl.K, pl.W);
+    const int64_t groups = ((pl.channels + 7) / 8) * 8 * (seq ? 1 : pl.nb);
     const int variant = sh->T % pl.P != 0 ? (seq ? kNewtonAnySeq : kNewtonAny)
                         : pl.nb == 1      ? kNewtonFullSingle
                                           : (seq ? kNewtonFullSeq : kNewtonFull);

@@ -736,18 +736,6 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         for (int kk = 0; kk < K; ++kk) tmp[kk] = vget(s[kk], c);
         store_steps<K>(A.s[c] + soff, t0, T, A.sst, A.s_vec != 0, tmp);
     }
-    // Block-sequential time blocks: hand the block's last state to the
-    // successor through the unit's record (device-coherent stores: the
-    // state planes' plain stores may sit in this XCD's L2, which another
-    // XCD does not see), then the stop flag (its store waits for them).
-    if constexpr (SEQ) {
-        if (last_lane_of_block) {
-            float *rec = A.records + unit * (int64_t)(A.cap + 1) * RF;
-#pragma unroll
-            for (int c = 0; c < S; ++c) store_relaxed(rec + c, vget(s[K - 1], c));
-            publish_flag(A.flags + unit, kStopBase + it);
-        }
-    }
     // The unit's own convergence record, folded into the info record by a
     // separate pass: atomics on one shared record from every workgroup
     // serialise on a single address and stall the whole solve.
@@ -755,20 +743,19 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         *reinterpret_cast<uint2 *>(A.unit_info + 2 * unit) = make_uint2(bmx, (uint32_t)it);
 }
 
-// One work unit per workgroup.  Serves every case: several time blocks per
-// channel (dynamic tickets), ragged T, warm starts.
-// SEQ (time blocks of many channels): block-sequential.  Block k > 0 waits
-// until block k-1 of its channel has converged and stored its states, then
-// solves its own Newton system from the exact state before it (block k-1's
-// last state, handed over in block k-1's record): no per-iteration carries
-// or look-back.  Every block
-// still stops only when its own max |r_t| < tol, the residual of its first
-// step taken against that state, so the whole trajectory meets the stopping
-// rule; the iterates differ from one Newton iteration over the whole
-// sequence, the converged states agree with it to within the tolerance.
-// Rank-spaced tickets hand a block out about when its predecessor ends, so
-// the wait is short; every predecessor holds a smaller ticket, so it is
-// resident or done and the waits cannot deadlock.
+// One work unit per workgroup, or (SEQ) every time block of one channel.
+// Serves every case: several time blocks per channel (dynamic tickets),
+// ragged T, warm starts.
+// SEQ (time blocks of many channels): block-sequential.  The workgroup
+// solves its channel's blocks one after the other, block k from the exact
+// state before it — block k-1's converged last state, handed from the last
+// lane to the first through LDS — with no per-iteration carries, look-back
+// or waits on other workgroups.  Every block still stops only when its own
+// max |r_t| < tol, the residual of its first step taken against that state,
+// so the whole trajectory meets the stopping rule; the iterates differ from
+// one Newton iteration over the whole sequence, the converged states agree
+// with it to within the tolerance.  Block k+1's projection loads are issued
+// as soon as block k's states are stored, so they overlap that store.
 template <class Cell, int K, int W, bool BF16, bool FULL, bool SINGLE, bool SEQ = false>
 __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>::kMinWavesPerEu))
     newton_kernel(SolveArgs A)
@@ -780,74 +767,80 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>
 
     __shared__ LoopSmem<Cell, K, W, kLdsMaps> sm;
     __shared__ int64_t s_ticket;
+    __shared__ V s_carry;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
 
     int64_t ch;
     int32_t k;
-    if (!SINGLE && A.nb > 1) {
+    if (!SINGLE && !SEQ && A.nb > 1) {
         take_unit(A.ticket, A.channels, A.nb, s_ticket, ch, k);
     } else {
         ch = xcd_channel(blockIdx.x, A.channels);
         k = 0;
     }
     if (ch >= A.channels) return;
-    const int64_t unit = ch * A.nb + k;
     const int64_t b = ch / A.D, d = ch - b * A.D;
     const int64_t T = A.T;
-    const int64_t tb0 = (int64_t)k * P;
-    const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
-
     const typename Cell::Coef cf = Cell::coef(A.a, A.D, d);
-    float u[K][G];
-    load_projections<Cell, K, BF16, FULL>(A, b * A.usb + d * A.usd, t0, u);
-
-    // Newton start and the lane's copy of the state just before it.
     const int64_t soff = b * A.ssb + d * A.ssd;
-    V s[K];
-    V hin = vzero<V>();
-    if (A.init_from_output) {
+    const int32_t k_end = SEQ ? A.nb : k + 1;
+    V carry = vzero<V>();  // (SEQ) block k-1's last state, for block k's first lane
+
+    for (; k < k_end; ++k) {
+        const int64_t unit = ch * A.nb + k;
+        const int64_t tb0 = (int64_t)k * P;
+        const int64_t t0 = tb0 + (int64_t)(wave * kWave + lane) * K;
+
+        float u[K][G];
+        load_projections<Cell, K, BF16, FULL>(A, b * A.usb + d * A.usd, t0, u);
+
+        // Newton start and the lane's copy of the state just before it.
+        V s[K];
+        V hin = vzero<V>();
+        if (A.init_from_output) {
 #pragma unroll
-        for (int c = 0; c < S; ++c) {
-            float tmp[K];
-            load_steps<K, false>(A.s[c], soff, t0, T, A.sst, A.s_vec != 0, tmp);
+            for (int c = 0; c < S; ++c) {
+                float tmp[K];
+                load_steps<K, false>(A.s[c], soff, t0, T, A.sst, A.s_vec != 0, tmp);
 #pragma unroll
-            for (int kk = 0; kk < K; ++kk) vset(s[kk], c, tmp[kk]);
+                for (int kk = 0; kk < K; ++kk) vset(s[kk], c, tmp[kk]);
+            }
+#pragma unroll
+            for (int c = 0; c < S; ++c) {
+                float x = 0.0f;
+                if (t0 == 0)
+                    x = A.s0[c][b * A.D + d];
+                else if (t0 == tb0)
+                    x = SEQ ? vget(carry, c) : A.hin0[unit * S + c];
+                else if (t0 - 1 < T)
+                    x = A.s[c][soff + (t0 - 1) * A.sst];
+                vset(hin, c, x);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) s[kk] = vzero<V>();
+            if (t0 == 0) {
+#pragma unroll
+                for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
+            } else if (SEQ && t0 == tb0) {
+                hin = carry;
+            }
         }
-#pragma unroll
-        for (int c = 0; c < S; ++c) {
-            float x = 0.0f;
-            if (t0 == 0)
-                x = A.s0[c][b * A.D + d];
-            else if (t0 == tb0)
-                x = A.hin0[unit * S + c];
-            else if (t0 - 1 < T)
-                x = A.s[c][soff + (t0 - 1) * A.sst];
-            vset(hin, c, x);
-        }
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < K; ++kk) s[kk] = vzero<V>();
-        if (t0 == 0) {
-#pragma unroll
-            for (int c = 0; c < S; ++c) vset(hin, c, A.s0[c][b * A.D + d]);
-        }
-    }
-    if constexpr (SEQ) {
-        if (k > 0 && wave == 0) {
-            const int32_t *pred = A.flags + unit - 1;
-            while (load_flag(pred) < kStopBase) __builtin_amdgcn_s_sleep(2);
-            after_flag();
-            if (lane == 0) {
-                const float *rec =
-                    A.records + (unit - 1) * (int64_t)(A.cap + 1) * MapRec<typename Cell::Map>::kFloats;
-#pragma unroll
-                for (int c = 0; c < S; ++c) vset(hin, c, load_relaxed(rec + c));
+        solve_unit<Cell, K, W, FULL, kLdsMaps, SINGLE, SEQ>(A, ch, k, cf, u, s, hin, sm);
+        if constexpr (SEQ) {
+            if (k + 1 < k_end) {
+                // the block's last state, from its last lane to every lane
+                // (the next block's first lane takes it); the barrier also
+                // orders this block's last LDS reads before the next block's
+                // first writes
+                if (wave == W - 1 && lane == kWave - 1) s_carry = s[K - 1];
+                __syncthreads();
+                carry = s_carry;
             }
         }
     }
-    solve_unit<Cell, K, W, FULL, kLdsMaps, SINGLE, SEQ>(A, ch, k, cf, u, s, hin, sm);
 }
 
 #ifdef PARARNN_DEFINE_AUX_KERNELS  // compiled once, in the ABI translation unit
