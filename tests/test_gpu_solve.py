@@ -364,3 +364,29 @@ def test_block_sequential_time_blocks(cell, T, dtype):
     ref = block_sequential_deer(cell, inp, 4096, cap)
     scale = max(1.0, max(float(np.abs(r).max()) for r in ref))
     assert max_err(capped, ref) < 1e-4 * scale
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("T", [8192, 9000])
+def test_block_sequential_warm_start(cell, T):
+    """Warm starts on the block-sequential path (1024 channels, blocks of
+    4096 steps chained in one workgroup, full and ragged last block): a start
+    at the oracle's trajectory stops with no update and returns it unchanged;
+    a perturbed start converges to the same trajectory, the first step of
+    every block after the first taken from its predecessor's converged state
+    rather than from the perturbed start."""
+    from nonlinear_rnn_amd import pararnn as pr
+    B, D = 1, 1024
+    assert pr.plan(cell, pr.make_shape(B, T, D))[2] == -(-T // 4096)
+    inp = make_inputs(cell, B, T, D, 7300 + T, s0_std=0.2, f_bias=1.0)
+    ref = oracle_states(inp)
+    start = [r.astype(np.float32) for r in ref]
+    got, info = gpu_solve(inp, 1e-5, 30, init=start)
+    assert info["converged"] and info["iters"] == 0
+    for g, s in zip(got, start):
+        assert np.array_equal(g, s)
+    rng = np.random.default_rng(6)
+    pert = [s + rng.standard_normal(s.shape).astype(np.float32) * 0.05 for s in start]
+    got, info = gpu_solve(inp, 1e-6, 30, init=pert)
+    assert info["converged"] and info["iters"] >= 1
+    assert max_err(got, ref) < TOL32
