@@ -49,6 +49,9 @@ constexpr int32_t kStopBase = 1 << 24;
 #ifndef PARARNN_GRU_K16_WAVES
 #define PARARNN_GRU_K16_WAVES 4
 #endif
+#ifndef PARARNN_LSTM_GATES_IN_LDS
+#define PARARNN_LSTM_GATES_IN_LDS 3
+#endif
 
 struct SolveArgs {
     const void *u[4];
@@ -428,13 +431,34 @@ struct MapStore {
         (kGru && PARARNN_GRU_MAPS_IN_LDS && K >= 8) ? K - 1
         : (!kGru && !SINGLE && K == 16) ? 8
                                                   : 0;
-    // register budget of the unmasked ParaGRU loop
-    // (everything else, ParaLSTM included: at most 256 VGPRs, two waves per
-    // SIMD; one more register would halve the occupancy)
+    // ParaLSTM with one block per channel (running compositions in VGPRs,
+    // LDS otherwise unused): the projections of its last kLdsGates gates
+    // wait in LDS between Newton evaluations (48 KB per 4-wave workgroup at
+    // K = 16), which brings the loop to the 168 VGPRs of three waves per
+    // SIMD.  With two gates there the loop spilled 21-25 registers; with
+    // all four the LDS would allow only two workgroups per CU.
+    static constexpr int kLdsGates =
+        (!kGru && SINGLE && FULL && K == 16 && W <= 4) ? PARARNN_LSTM_GATES_IN_LDS : 0;
+    // register budget of the unmasked ParaGRU loop and of the ParaLSTM loop
+    // above (everything else: at most 256 VGPRs, two waves per SIMD; one
+    // more register would halve the occupancy)
     static constexpr int kMinWavesPerEu =
-        !(kGru && kLdsMaps > 0 && FULL && K <= 16) ? 2
-        : (K == 16 && W <= 4)                      ? PARARNN_GRU_K16_WAVES
-                                                   : 4;
+        kLdsGates > 0                                ? 3
+        : !(kGru && kLdsMaps > 0 && FULL && K <= 16) ? 2
+        : (K == 16 && W <= 4)                        ? PARARNN_GRU_K16_WAVES
+                                                     : 4;
+};
+
+// Projections of the last NG gates of every step in LDS, as 16-byte groups
+// of four steps, one plane per (group, gate) so that a wave's accesses are
+// consecutive 16-byte words.
+template <int K, int NG, int N>
+struct GateLds {
+    float4 v[K / 4][NG][N];
+};
+template <int K, int N>
+struct GateLds<K, 0, N> {
+    float4 v[1][1][1];
 };
 
 // A running composition in LDS, one plane of floats per map component so
@@ -532,12 +556,13 @@ __device__ __forceinline__ void load_projections(const SolveArgs &A, int64_t uof
 // before its first step and the Newton start `s`; writes the converged states
 // and folds the unit into the info record.
 // SEQ: block-sequential time blocks (no carries; see newton_kernel).
-template <class Cell, int K, int W, bool FULL, int NL, bool SINGLE, bool SEQ>
+template <class Cell, int K, int W, bool FULL, int NL, bool SINGLE, bool SEQ, int NG = 0>
 __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32_t k,
                                            const typename Cell::Coef &cf,
                                            const float (&u)[K][Cell::G],
                                            typename Cell::Vec (&s)[K], typename Cell::Vec hin,
-                                           LoopSmem<Cell, K, W, NL> &sm)
+                                           LoopSmem<Cell, K, W, NL> &sm,
+                                           const GateLds<K, NG, W * kWave> *ug = nullptr)
 {
     using M = typename Cell::Map;
     using V = typename Cell::Vec;
@@ -554,6 +579,26 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
     const bool multi = !SINGLE && !SEQ && A.nb > 1;
     const bool last_lane_of_block = (wave == W - 1) && (lane == kWave - 1);
     const bool full = FULL || tb0 + P <= T;  // uniform over the workgroup
+
+    // step kk's projections: the first G - NG gates from registers, the
+    // rest from LDS
+    constexpr int G = Cell::G;
+    struct Proj {
+        float v[G];
+    };
+    const auto proj = [&](int kk) {
+        Proj p;
+#pragma unroll
+        for (int g = 0; g < G - NG; ++g) p.v[g] = u[kk][g];
+        if constexpr (NG > 0) {
+#pragma unroll
+            for (int g = G - NG; g < G; ++g) {
+                const float4 q = ug->v[kk / 4][g - (G - NG)][threadIdx.x];
+                p.v[g] = (kk % 4 == 0) ? q.x : (kk % 4 == 1) ? q.y : (kk % 4 == 2) ? q.z : q.w;
+            }
+        }
+        return p;
+    };
 
     const uint32_t tolb = __float_as_uint(A.tol);
     // Newton converges quadratically: once max|r| < sqrt(tol) (A.guess_tol)
@@ -604,7 +649,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
             V prev = (SINGLE || SEQ) ? hin : opaque(hin);
 #pragma unroll
             for (int kk = 0; kk < K; ++kk) {
-                V rk = Cell::step_residual(cf, u[kk], prev, s[kk]);
+                V rk = Cell::step_residual(cf, proj(kk).v, prev, s[kk]);
                 if (!full) rk = keep_or_zero(rk, t0 + kk < T);
                 mxf = resmax(mxf, rk);
                 prev = (SINGLE || SEQ) ? s[kk] : opaque(s[kk]);
@@ -652,7 +697,7 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
         };
         const auto up_all = [&]() {
 #pragma unroll
-            for (int kk = 0; kk < K; ++kk) up(kk, Cell::step_map(cf, u[kk], prev, s[kk]));
+            for (int kk = 0; kk < K; ++kk) up(kk, Cell::step_map(cf, proj(kk).v, prev, s[kk]));
         };
         // (the carry-exchanging kernels would spill with the second loop)
         if constexpr (Cell::kZeroPass && (SINGLE || SEQ)) {
@@ -660,9 +705,9 @@ __device__ __forceinline__ void solve_unit(const SolveArgs &A, int64_t ch, int32
                 // first evaluation from the zero start: every step but the
                 // lane's first (whose predecessor may be a given state) sees
                 // h_{t-1} = h_t = 0
-                up(0, Cell::step_map(cf, u[0], prev, s[0]));
+                up(0, Cell::step_map(cf, proj(0).v, prev, s[0]));
 #pragma unroll
-                for (int kk = 1; kk < K; ++kk) up(kk, Cell::step_map_zero(cf, u[kk]));
+                for (int kk = 1; kk < K; ++kk) up(kk, Cell::step_map_zero(cf, proj(kk).v));
             } else {
                 up_all();
             }
@@ -764,10 +809,12 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>
     constexpr int G = Cell::G, S = Cell::S;
     constexpr int P = W * kWave * K;
     constexpr int kLdsMaps = MapStore<Cell, K, W, FULL, SINGLE>::kLdsMaps;
+    constexpr int NG = MapStore<Cell, K, W, FULL, SINGLE>::kLdsGates;
 
     __shared__ LoopSmem<Cell, K, W, kLdsMaps> sm;
     __shared__ int64_t s_ticket;
     __shared__ V s_carry;
+    __shared__ GateLds<K, NG, W * kWave> ug;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -795,6 +842,15 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>
 
         float u[K][G];
         load_projections<Cell, K, BF16, FULL>(A, b * A.usb + d * A.usd, t0, u);
+        if constexpr (NG > 0) {
+            // (each lane reads back only its own words, so no barrier)
+#pragma unroll
+            for (int q = 0; q < K / 4; ++q)
+#pragma unroll
+                for (int g = G - NG; g < G; ++g)
+                    ug.v[q][g - (G - NG)][threadIdx.x] =
+                        make_float4(u[4 * q][g], u[4 * q + 1][g], u[4 * q + 2][g], u[4 * q + 3][g]);
+        }
 
         // Newton start and the lane's copy of the state just before it.
         V s[K];
@@ -828,7 +884,7 @@ __global__ void __launch_bounds__(W * kWave, (MapStore<Cell, K, W, FULL, SINGLE>
                 hin = carry;
             }
         }
-        solve_unit<Cell, K, W, FULL, kLdsMaps, SINGLE, SEQ>(A, ch, k, cf, u, s, hin, sm);
+        solve_unit<Cell, K, W, FULL, kLdsMaps, SINGLE, SEQ, NG>(A, ch, k, cf, u, s, hin, sm, &ug);
         if constexpr (SEQ) {
             if (k + 1 < k_end) {
                 // the block's last state, from its last lane to every lane
