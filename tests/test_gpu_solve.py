@@ -390,3 +390,27 @@ def test_block_sequential_warm_start(cell, T):
     got, info = gpu_solve(inp, 1e-6, 30, init=pert)
     assert info["converged"] and info["iters"] >= 1
     assert max_err(got, ref) < TOL32
+
+
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("T,W", [(4096, 4), (2048, 2)])
+def test_warm_start_full_single_blocks(cell, T, W):
+    """Warm starts on full one-block-per-channel tiles (K = 16), the kernels
+    whose ParaLSTM form keeps three gates' projections in LDS: a start at
+    the oracle's trajectory stops with no update and returns it unchanged;
+    a perturbed start converges to the same trajectory."""
+    from nonlinear_rnn_amd import pararnn as pr
+    B, D = 2, 128
+    assert pr.plan(cell, pr.make_shape(B, T, D)) == (16, W, 1)
+    inp = make_inputs(cell, B, T, D, 7400 + T, s0_std=0.2, f_bias=1.0)
+    ref = oracle_states(inp)
+    start = [r.astype(np.float32) for r in ref]
+    got, info = gpu_solve(inp, 1e-6, 20, init=start)
+    assert info["converged"] and info["iters"] == 0
+    for g, s in zip(got, start):
+        assert np.array_equal(g, s)
+    rng = np.random.default_rng(7)
+    pert = [s + rng.standard_normal(s.shape).astype(np.float32) * 0.05 for s in start]
+    got, info = gpu_solve(inp, 1e-6, 20, init=pert)
+    assert info["converged"] and info["iters"] >= 1
+    assert max_err(got, ref) < TOL32
