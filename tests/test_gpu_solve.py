@@ -61,6 +61,26 @@ def test_per_iteration_parity_with_deer(cell, KW, iters):
     assert max_err(got, ref) < 1e-4 * scale
 
 
+@pytest.mark.parametrize("cell", ["gru", "lstm"])
+@pytest.mark.parametrize("W", [1, 2, 4])
+@pytest.mark.parametrize("iters", [1, 3])
+def test_per_iteration_parity_full_single_blocks(cell, W, iters):
+    """The same on full one-block-per-channel tiles (K = 16, T = 1024 W):
+    the kernels that take the zero-start pass (ParaGRU) and keep three
+    gates' projections in LDS (ParaLSTM)."""
+    T = 64 * 16 * W
+    inp = make_inputs(cell, 1, T, 4, 3100 + 10 * W + iters, s0_std=0.3, f_bias=1.0)
+    got, info = gpu_solve(inp, 0.0, iters, 16, W)
+    assert info["iters"] == iters and not info["converged"] and info["units"] == 4
+    u = deer.from_planes(inp.u)
+    a = deer.a_per_channel(inp.a, 1)
+    s0 = np.stack([p.reshape(-1).astype(np.float64) for p in inp.s0], -1)
+    s, _ = deer.newton(cell, u, a, s0, tol=0.0, max_iters=iters)
+    ref = [s[..., c].reshape(1, 4, T) for c in range(s.shape[-1])]
+    scale = max(1.0, max(float(np.abs(r).max()) for r in ref))
+    assert max_err(got, ref) < 1e-4 * scale
+
+
 def test_linear_gru_converges_in_one_update():
     inp = make_inputs("gru", 2, 3000, 8, 41, s0_std=0.5)
     inp.a[:] = 0
