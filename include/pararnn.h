@@ -119,7 +119,9 @@ typedef struct {
  * problem and tiling (0 is possible).  Returns 0 on a bad argument too; the
  * solve itself reports the error.  For the adjoint pass adjoint = 1.
  * For a solve the figure counts the time-block hand-off (several blocks per
- * channel), 8 bytes per work unit for the convergence records an info
+ * channel that run side by side, i.e. fewer than 1024 channels; with more, a
+ * channel's blocks are solved one after the other inside one workgroup and
+ * need none), 8 bytes per work unit for the convergence records an info
  * record is folded from, and the staging room of planes that are not
  * time-contiguous; a solve without an info record, on time-contiguous
  * planes with one block per channel, runs with no workspace at all. */

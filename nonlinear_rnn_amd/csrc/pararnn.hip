@@ -163,16 +163,28 @@ pararnn_status_t make_plan(pararnn_cell_t cell, const pararnn_shape_t *sh,
 // record is requested).
 struct SolveWs {
     size_t ticket = 0, flags = 0, records = 0, hin0 = 0;
-    size_t multi = 0;      // bytes of the hand-off part (0 with one block per channel)
+    size_t multi = 0;      // bytes of the hand-off part (0 with one block per channel
+                           // and for block-sequential solves)
     size_t unit_info = 0;  // offset of the per-unit records, 8 bytes a unit
     size_t total = 0;
 };
+
+// With a full ticket group of channels (more workgroups than the device
+// holds at once) every workgroup solves one channel's time blocks one after
+// the other, each from its predecessor's converged last state: no
+// per-iteration carries, tickets or flags, so no hand-off workspace.  With
+// fewer channels a channel's blocks run side by side, in workgroups of their
+// own, as one Newton iteration over the whole sequence.
+bool block_sequential(const Plan &pl)
+{
+    return pl.nb > 1 && (pl.channels + 7) / 8 * 8 >= kTicketGroup && newton_seq_built(pl.K, pl.W);
+}
 
 SolveWs solve_ws_layout(pararnn_cell_t cell, const Plan &pl, const pararnn_newton_t *opt)
 {
     SolveWs w;
     size_t off = 0;
-    if (pl.nb > 1) {
+    if (pl.nb > 1 && !block_sequential(pl)) {
         const int64_t cap = opt ? opt->max_iters : 0;
         w.ticket = off;
         off += kAlign;
@@ -280,14 +292,7 @@ pararnn_status_t solve_core(pararnn_cell_t cell, const pararnn_shape_t *sh, cons
     };
     if (!work) return fold_info();
 
-    // With a full ticket group of channels (more workgroups than the device
-    // holds at once) every workgroup solves one channel's time blocks one
-    // after the other, each from its predecessor's converged last state (no
-    // per-iteration carries, no tickets or flags).  With fewer channels a
-    // channel's blocks run side by side, in workgroups of their own, as one
-    // Newton iteration over the whole sequence.
-    const bool seq = pl.nb > 1 && (pl.channels + 7) / 8 * 8 >= kTicketGroup &&
-                     newton_seq_built(pl.K, pl.W);
+    const bool seq = block_sequential(pl);
     if (pl.nb > 1 && !seq) {
         const int tpb = 256;
         hipLaunchKernelGGL(solve_init_kernel, dim3((unsigned)((pl.units + tpb - 1) / tpb)),

@@ -94,14 +94,25 @@ def test_workspace_sizes():
     n = pr.make_newton(1e-6, 20)
     # one block per channel: only the per-unit convergence records
     assert pr.workspace_bytes("gru", pr.make_shape(8, 4096, 1024), n) == 8192 * 8
-    ws = pr.workspace_bytes("gru", pr.make_shape(4, 16384, 4096), n)
-    units = 4 * 4096 * 2  # two 8192-step blocks per channel
-    assert ws >= units * 4 + units * 21 * 4 * 4
-    ws2 = pr.workspace_bytes("gru", pr.make_shape(4, 16384, 4096), pr.make_newton(1e-6, 20,
-                             init_from_output=True))
-    assert ws2 >= ws + units * 4
-    wl = pr.workspace_bytes("lstm", pr.make_shape(4, 16384, 4096), n)
-    assert wl > ws
+    # 16,384 channels of four 4096-step blocks, solved block-sequentially
+    # inside one workgroup a channel: no hand-off, only the per-unit records
+    units = 4 * 4096 * 4
+    assert pr.plan("gru", pr.make_shape(4, 16384, 4096)) == (16, 4, 4)
+    for cell in ("gru", "lstm"):
+        for init in (False, True):
+            assert pr.workspace_bytes(cell, pr.make_shape(4, 16384, 4096),
+                                      pr.make_newton(1e-6, 20, init_from_output=init)) == units * 8
+    # 64 channels: the blocks run side by side and exchange carries (flags,
+    # per-iteration records of S + S^2 + 1 floats, boundary states of a warm
+    # start)
+    sh = pr.make_shape(1, 16384, 64)
+    few = 64 * 4
+    assert pr.plan("gru", sh) == (16, 4, 4)
+    ws = pr.workspace_bytes("gru", sh, n)
+    assert ws >= few * 4 + few * 21 * 3 * 4 + few * 8
+    ws2 = pr.workspace_bytes("gru", sh, pr.make_newton(1e-6, 20, init_from_output=True))
+    assert ws2 >= ws + few * 4
+    assert pr.workspace_bytes("lstm", sh, n) > ws
     wa = pr.workspace_bytes("lstm", pr.make_shape(16, 2048, 4096), n, adjoint=True)
     assert wa >= 16 * 4096 * 4 * 4
     assert pr.workspace_bytes(7, pr.make_shape(1, 1, 1), n) == 0
