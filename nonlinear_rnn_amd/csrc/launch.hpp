@@ -57,8 +57,8 @@ hipError_t launch_scan(int S, int K, int W, bool reverse, int64_t groups, hipStr
 // Newton kernel variants: 0 = any block (ragged T), 1 = blocks wholly inside
 // [0, T), 2 = as 1 with one block per channel (no cross-block code); 3 and 4
 // = 0 and 1 with block-sequential time blocks (built for K = 16, W = 4 only:
-// the long-sequence default with many channels, whose blocks are handed out
-// about when their predecessors end).
+// the long-sequence default with many channels, each workgroup solving one
+// channel's blocks in order).
 enum {
     kNewtonAny = 0,
     kNewtonFull = 1,
